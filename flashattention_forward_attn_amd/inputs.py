@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the HIP path's callers and by the oracle's callers.
+It holds random draws, the fp32 -> bf16 round-to-nearest-even conversion and
+the workload table, and none of the attention arithmetic.
+
+Tensor layout follows the [b, h, seq, d] shape used for Q, K and V in
+"谁偷走了 5090 的算力和显存" (the attention section, eager attention in five
+steps): contiguous, row-major, d fastest.
+
+Draw order for every workload: Q, K, V (each a float64 standard normal of
+shape (B, H, N, d), cast to float32), then, for the key-padding workload, the
+per-batch valid lengths, the batch item that gets a fully masked query block,
+and that block's start.  All draws come from ``numpy.random.default_rng(seed)``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Optional
+
+import numpy as np
+
+# Rows of the query block that the key-padding workload masks out entirely.
+MASKED_QUERY_BLOCK = 128
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    NaN inputs are not expected (the generators never produce them).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the exact fp32 values they encode."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 value, returned as fp32."""
+    return bf16_to_f32(bf16_bits(x))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "bf16" or "f32"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    qk_mult: float = 1.0        # Q and K draws are multiplied by this before rounding
+    v_dist: str = "normal"      # "normal": N(0,1); "uniform": U(-1, 1)
+    key_padding: bool = False   # per-batch valid key length plus one fully masked query block
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def flops(self) -> float:
+        """Nominal forward FLOPs: two N x N x d contractions per head, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def describe(self) -> dict:
+        return dataclasses.asdict(self)
+
+
+# The five workloads the method is measured on (fp32 single head; bf16
+# non-causal; bf16 causal; bf16 causal long context; bf16 key-padding stress).
+WORKLOADS = {
+    "f32_b1h1n256d64": Workload("f32_b1h1n256d64", "f32", 1, 1, 256, 64, False),
+    "bf16_b4h16n2048d64": Workload("bf16_b4h16n2048d64", "bf16", 4, 16, 2048, 64, False),
+    "bf16_causal_b2h32n4096d128": Workload("bf16_causal_b2h32n4096d128", "bf16", 2, 32, 4096, 128, True),
+    "bf16_causal_b1h16n16384d128": Workload("bf16_causal_b1h16n16384d128", "bf16", 1, 16, 16384, 128, True),
+    "bf16_keypad_b8h32n1024d128": Workload("bf16_keypad_b8h32n1024d128", "bf16", 8, 32, 1024, 128, False,
+                                           qk_mult=8.0, v_dist="uniform", key_padding=True),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host copies of one workload's inputs.
+
+    q, k, v are fp32 arrays of shape (B, H, N, d).  For bf16 workloads every
+    value is exactly representable in bf16 and ``*_bits`` hold the bf16 bit
+    patterns the device receives; for fp32 workloads ``*_bits`` are None.
+    kv_limit is None or an int32 array of shape (B, N): query row i of batch
+    item b may attend to keys j < kv_limit[b, i].
+    """
+    workload: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    kv_limit: Optional[np.ndarray]
+    q_bits: Optional[np.ndarray] = None
+    k_bits: Optional[np.ndarray] = None
+    v_bits: Optional[np.ndarray] = None
+    lengths: Optional[np.ndarray] = None
+    masked_batch: Optional[int] = None
+    masked_q0: Optional[int] = None
+
+    def digests(self) -> dict:
+        out = {}
+        for name in ("q", "k", "v", "kv_limit"):
+            a = getattr(self, name)
+            if a is not None:
+                out[name] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+        return out
+
+
+def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
+    """Draw one workload's inputs (see the module docstring for the draw order)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = (rng.standard_normal(shape).astype(np.float32)) * np.float32(w.qk_mult)
+    k = (rng.standard_normal(shape).astype(np.float32)) * np.float32(w.qk_mult)
+    if w.v_dist == "normal":
+        v = rng.standard_normal(shape).astype(np.float32)
+    elif w.v_dist == "uniform":
+        v = rng.uniform(-1.0, 1.0, shape).astype(np.float32)
+    else:
+        raise ValueError(f"unknown v_dist {w.v_dist!r}")
+
+    kv_limit = lengths = masked_batch = masked_q0 = None
+    if w.key_padding:
+        lengths = rng.integers(1, w.N + 1, size=w.B).astype(np.int32)
+        masked_batch = int(rng.integers(0, w.B))
+        n_blocks = -(-w.N // MASKED_QUERY_BLOCK)
+        masked_q0 = int(rng.integers(0, n_blocks)) * MASKED_QUERY_BLOCK
+        kv_limit = np.repeat(lengths[:, None], w.N, axis=1).astype(np.int32)
+        kv_limit[masked_batch, masked_q0:masked_q0 + MASKED_QUERY_BLOCK] = 0
+
+    if w.dtype == "bf16":
+        qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+        return Inputs(w, bf16_to_f32(qb), bf16_to_f32(kb), bf16_to_f32(vb), kv_limit,
+                      qb, kb, vb, lengths, masked_batch, masked_q0)
+    if w.dtype == "f32":
+        return Inputs(w, q, k, v, kv_limit, None, None, None, lengths, masked_batch, masked_q0)
+    raise ValueError(f"unknown dtype {w.dtype!r}")
+
+
+def custom(name: str, dtype: str, B: int, H: int, N: int, d: int, causal: bool, **kw) -> Workload:
+    """A workload of any shape, for parity sweeps over odd sizes."""
+    return Workload(name, dtype, B, H, N, d, causal, **kw)
+
+
+def random_kv_limit(B: int, N: int, seed: int, kind: str) -> np.ndarray:
+    """Per-row key limits for mask sweeps: 'random' (each row uniform in [0, N]),
+    'zeros' (every row fully masked), 'some_zero' (random, with every fifth row 0)."""
+    rng = np.random.default_rng(seed)
+    if kind == "zeros":
+        return np.zeros((B, N), np.int32)
+    lim = rng.integers(0, N + 1, size=(B, N)).astype(np.int32)
+    if kind == "some_zero":
+        lim[:, ::5] = 0
+    elif kind != "random":
+        raise ValueError(kind)
+    return lim

@@ -1,0 +1,137 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import this package.  The product path (the HIP library and its Python
+binding) never imports, links or calls anything here, and this package imports
+nothing from the product.
+
+The arithmetic lives in ``fa_oracle.c`` (plain C, fp64, OpenMP over rows); this
+module compiles it with gcc and calls it through ctypes.  What it computes and
+which passages it follows are stated in the header of ``fa_oracle.c``:
+O = softmax(scale * Q K^T + M) V and LSE = log sum exp(scale * Q K^T + M) per
+row, M being 0 on valid keys and -inf elsewhere, a row with no valid key giving
+O = 0 and LSE = -inf.
+
+Parity: every function here is pinned by ``tests/test_oracle.py`` against the
+pages' worked examples, closed forms, invariants and brute force; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "fa_oracle.c")
+LIBRARY = os.path.join(_HERE, "libfa_oracle.so")
+
+_lib = None
+
+
+def compile_library(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", source, "-o", output, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def load(path: str = LIBRARY):
+    """Load a compiled oracle library and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.fa_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                  ctypes.c_int, ctypes.c_double, ip, ctypes.c_int]
+    lib.fa_oracle_fwd.restype = ctypes.c_int
+    lib.fa_oracle_rows.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                   ctypes.c_int, ctypes.c_double, ip, i64, lp, ctypes.c_int]
+    lib.fa_oracle_rows.restype = ctypes.c_int
+    lib.fa_oracle_max_threads.argtypes = []
+    lib.fa_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _library():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            compile_library()
+        _lib = load(LIBRARY)
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _limits(kv_limit, B: int, N: int):
+    if kv_limit is None:
+        return None, None
+    lim = np.ascontiguousarray(kv_limit, dtype=np.int32)
+    if lim.shape != (B, N):
+        raise ValueError(f"kv_limit must have shape {(B, N)}, got {lim.shape}")
+    return lim, _ptr(lim, ctypes.c_int32)
+
+
+def attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
+              kv_limit=None, nthreads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Every row of attention for q, k, v of shape (B, H, N, d).
+
+    Returns (o, lse): o float64 (B, H, N, d), lse float64 (B, H, N), natural log.
+    scale defaults to 1/sqrt(d).
+    """
+    lib = lib or _library()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one (B, H, N, d) shape")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lim, lim_p = _limits(kv_limit, B, N)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), np.float64)
+    rc = lib.fa_oracle_fwd(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                           _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                           B, H, N, d, int(bool(causal)), float(scale), lim_p, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd failed ({rc})")
+    return o, lse
+
+
+def attention_rows(q, k, v, row_ids, causal: bool = False, scale: Optional[float] = None,
+                   kv_limit=None, nthreads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected rows only.  row_ids are flat indices (b * H + h) * N + i.
+
+    Returns (o, lse) of shapes (len(row_ids), d) and (len(row_ids),).
+    """
+    lib = lib or _library()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    lim, lim_p = _limits(kv_limit, B, N)
+    o = np.empty((ids.size, d), np.float64)
+    lse = np.empty((ids.size,), np.float64)
+    rc = lib.fa_oracle_rows(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                            _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                            B, H, N, d, int(bool(causal)), float(scale), lim_p,
+                            ids.size, _ptr(ids, ctypes.c_int64), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_rows failed ({rc})")
+    return o, lse
+
+
+def max_threads() -> int:
+    return int(_library().fa_oracle_max_threads())
