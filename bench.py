@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+One step = one fused forward (one kernel launch) over the whole workload with
+inputs already resident in device memory.  Default workload: bf16, causal,
+B=2, H=32, N=4096, d=128 (the shape the >= 50 % of MFMA peak target is set
+on).  FLOPs per step follow the metric's convention: 4*B*H*N^2*d, halved for
+causal.  Prints ONE JSON line.
+
+Besides the headline number the line carries:
+  roofline     -- achieved TFLOP/s of the fused kernel (algorithmic FLOPs per
+                  launch / mean launch time from HIP events on the launch
+                  stream) against the bf16 dense MFMA peak of 2500 TFLOP/s;
+  cpu_baseline -- the fp64 oracle timed on the host cores on a bounded,
+                  evenly spaced sample of the same workload's query rows,
+                  scaled to TFLOP/s with the same FLOP convention;
+  unfused      -- the three-kernel baseline (S and P through device memory)
+                  timed the same way;
+  workloads    -- the other bf16 workloads, fused, timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HEADLINE = "bf16_causal_b2h32n4096d128"
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def device_inputs(torch, x):
+    if x.workload.dtype == "bf16":
+        def dev(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        q, k, v = dev(x.q_bits), dev(x.k_bits), dev(x.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(a).cuda() for a in (x.q, x.k, x.v))
+    lim = None if x.kv_limit is None else torch.from_numpy(x.kv_limit).cuda()
+    return q, k, v, lim
+
+
+def time_launches(torch, launch, steps: int, warmup: int) -> float:
+    """Mean milliseconds per launch, HIP events on the current (launch) stream."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        launch()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def measure_fused(torch, binding, x, steps, warmup):
+    w = x.workload
+    q, k, v, lim = device_inputs(torch, x)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    fn = binding.fa_fwd_bf16 if w.dtype == "bf16" else binding.fa_fwd_f32
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        fn(q, k, v, o, lse, w.causal, w.scale, lim, stream)
+
+    ms = time_launches(torch, launch, steps, warmup)
+    del q, k, v, o, lse, lim
+    return ms
+
+
+def measure_unfused(torch, binding, x, steps, warmup):
+    w = x.workload
+    q, k, v, lim = device_inputs(torch, x)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(binding.fa_unfused_workspace_bytes(w.B, w.H, w.N, 2), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        binding.fa_fwd_unfused_bf16(q, k, v, o, lse, w.causal, w.scale, lim, ws, stream)
+
+    ms = time_launches(torch, launch, steps, warmup)
+    del q, k, v, o, lse, lim, ws
+    return ms
+
+
+def effective_flops(x) -> float:
+    """FLOPs of the valid (query, key) pairs only: 4 d per pair."""
+    w = x.workload
+    i = np.arange(w.N, dtype=np.int64)
+    lim = np.full((w.B, w.N), w.N, np.int64) if x.kv_limit is None else np.minimum(x.kv_limit.astype(np.int64), w.N)
+    if w.causal:
+        lim = np.minimum(lim, i[None, :] + 1)
+    return float(4.0 * w.d * w.H * lim.sum())
+
+
+def cpu_baseline(x, target_seconds: float):
+    """Oracle on an evenly spaced sample of query rows, calibrated to about target_seconds."""
+    import oracle
+    w = x.workload
+    threads = host_threads()
+    rows_total = w.B * w.H * w.N
+    flops_per_row = w.flops() / rows_total
+    n_cal = min(rows_total, 4 * threads)
+    ids = np.linspace(0, rows_total - 1, n_cal).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention_rows(x.q, x.k, x.v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
+    cal = time.perf_counter() - t0
+    n = int(min(rows_total, max(n_cal, n_cal * target_seconds / max(cal, 1e-6))))
+    ids = np.unique(np.linspace(0, rows_total - 1, n).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.attention_rows(x.q, x.k, x.v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": ids.size * flops_per_row / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{ids.size} of {rows_total} query rows of {w.name}, evenly spaced, fp64, "
+                  f"{dt:.1f} s; FLOPs per row = workload FLOPs / rows",
+        "seconds": round(dt, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the unfused baseline and other workloads")
+    ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                      "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward pass shards over (batch, head) with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from flashattention_forward_attn_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    binding.load()
+
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.generate(w)
+    ms = measure_fused(torch, binding, x, args.steps, args.warmup)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f).get(w.name)
+        if t and t.get("kernel_source_sha256") == _kernel_digest():
+            traffic = t.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": "1/sqrt(d)", "flops_per_step": w.flops(), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_extras:
+        ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
+        line["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
+                           "fused_speedup": round(ums / ms, 2)}
+        others = {}
+        for name, ow in inputs.WORKLOADS.items():
+            if name == w.name or ow.dtype != "bf16":
+                continue
+            ox = inputs.generate(ow)
+            oms = measure_fused(torch, binding, ox, args.steps, args.warmup)
+            entry = {"ms": round(oms, 5), "TFLOP/s": round(ow.flops() / (oms * 1e-3) / 1e12, 2),
+                     "frac": round(ow.flops() / (oms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            if ox.kv_limit is not None:
+                entry["effective_TFLOP/s"] = round(effective_flops(ox) / (oms * 1e-3) / 1e12, 2)
+            others[name] = entry
+            del ox
+        line["workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _kernel_digest() -> str:
+    import hashlib
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "flashattention_forward_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(here)):
+        with open(os.path.join(here, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,149 @@
+"""ctypes binding of libfa.so: the C ABI of include/fa.h, one Python function per
+C entry point, with the same names.  Argument marshalling only: tensors become
+device pointers and sizes, torch's current stream becomes the hipStream_t, and
+a non-zero status becomes an exception.  Every step of the computation runs in
+the library's HIP kernels.
+
+The library is loaded on first use; if it is missing this raises (there is no
+fallback of any kind).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
+                5: "FA_ERR_ALIGN", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIAS"}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path: str = LIBRARY):
+    """Load libfa.so and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m flashattention_forward_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd_bf16.argtypes = fwd
+    lib.fa_fwd_f32.argtypes = fwd
+    lib.fa_fwd_unfused_bf16.argtypes = fwd[:-1] + [vp, sz, vp]
+    lib.fa_fwd_unfused_f32.argtypes = fwd[:-1] + [vp, sz, vp]
+    for name in ("fa_fwd_bf16", "fa_fwd_f32", "fa_fwd_unfused_bf16", "fa_fwd_unfused_f32"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fa_unfused_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_unfused_workspace_bytes.restype = sz
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load().fa_status_str(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        raise FAError(status, fa_status_str(status))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return int(stream.cuda_stream) or None
+
+
+def _dims(q):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def fa_fwd_bf16(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, stream=None) -> None:
+    """Fused forward, bf16 tensors [B, H, N, d]; lse fp32 [B, H, N]; kv_limit int32 [B, N] or None."""
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                              float(scale), _ptr(kv_limit), _stream(stream)))
+
+
+def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, stream=None) -> None:
+    """Fused forward, fp32 tensors [B, H, N, d]."""
+    B, H, N, d = _dims(q)
+    _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                             float(scale), _ptr(kv_limit), _stream(stream)))
+
+
+def fa_unfused_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
+    return int(load().fa_unfused_workspace_bytes(B, H, N, elem_bytes))
+
+
+def fa_fwd_unfused_bf16(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, workspace=None,
+                        stream=None) -> None:
+    """Unfused three-kernel forward (bf16); workspace is a device uint8 tensor."""
+    B, H, N, d = _dims(q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().fa_fwd_unfused_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                      int(bool(causal)), float(scale), _ptr(kv_limit), _ptr(workspace), nbytes,
+                                      _stream(stream)))
+
+
+def fa_fwd_unfused_f32(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, workspace=None,
+                       stream=None) -> None:
+    """Unfused three-kernel forward (fp32)."""
+    B, H, N, d = _dims(q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().fa_fwd_unfused_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                     int(bool(causal)), float(scale), _ptr(kv_limit), _ptr(workspace), nbytes,
+                                     _stream(stream)))
+
+
+def attention(q, k, v, causal: bool = False, scale: Optional[float] = None, kv_limit=None, unfused: bool = False,
+              stream=None):
+    """Allocate O and LSE with torch and run the fused (or unfused) forward.
+
+    q, k, v: contiguous device tensors [B, H, N, d], all bf16 or all fp32.
+    Returns (o, lse).  The unfused path also allocates its workspace.
+    """
+    import torch
+    B, H, N, d = _dims(q)
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        if unfused:
+            ws = torch.empty(fa_unfused_workspace_bytes(B, H, N, 2), dtype=torch.uint8, device=q.device)
+            fa_fwd_unfused_bf16(q, k, v, o, lse, causal, scale, kv_limit, ws, stream)
+        else:
+            fa_fwd_bf16(q, k, v, o, lse, causal, scale, kv_limit, stream)
+    elif q.dtype == torch.float32:
+        if unfused:
+            ws = torch.empty(fa_unfused_workspace_bytes(B, H, N, 4), dtype=torch.uint8, device=q.device)
+            fa_fwd_unfused_f32(q, k, v, o, lse, causal, scale, kv_limit, ws, stream)
+        else:
+            fa_fwd_f32(q, k, v, o, lse, causal, scale, kv_limit, stream)
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return o, lse

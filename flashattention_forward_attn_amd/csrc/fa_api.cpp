@@ -1,0 +1,143 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation on the
+// host, then dispatch to the HIP launchers.  No allocation, no synchronisation,
+// no global state, no exception crosses the boundary.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common checks for every entry point.  elem = bytes per q/k/v/o element.
+fa_status validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                   int N, int d, float scale, const int32_t* kv_limit, int elem) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    const int64_t elems = (int64_t)B * H * N * d;
+    if (elems > INT32_MAX) return FA_ERR_SHAPE;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        (kv_limit && !aligned(kv_limit, 4)))
+        return FA_ERR_ALIGN;
+    const int64_t tbytes = elems * elem;
+    const Range rq = span(q, tbytes), rk = span(k, tbytes), rv = span(v, tbytes), ro = span(o, tbytes);
+    const Range rl = span(lse, (int64_t)B * H * N * 4);
+    const Range rm = span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0);
+    for (Range in : {rq, rk, rv, rm}) {
+        if (overlap(ro, in) || overlap(rl, in)) return FA_ERR_ALIAS;
+    }
+    if (overlap(ro, rl)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+size_t workspace_bytes(int B, int H, int N, int elem) {
+    if (B < 1 || H < 1 || N < 1 || (elem != 2 && elem != 4)) return 0;
+    typedef unsigned __int128 u128;
+    const u128 rows = (u128)B * (u128)H * (u128)N * (u128)fa::unfused_ld(N);
+    const u128 total = ((rows * 4 + kWsAlign - 1) / kWsAlign) * kWsAlign +
+                       ((rows * (u128)elem + kWsAlign - 1) / kWsAlign) * kWsAlign;
+    if (total > (u128)SIZE_MAX) return 0;
+    return (size_t)total;
+}
+
+fa_status unfused(bool bf16_path, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, int causal, float scale, const int32_t* kv_limit, void* workspace,
+                  size_t workspace_bytes_given, void* stream) {
+    const int elem = bf16_path ? 2 : 4;
+    fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, kv_limit, elem);
+    if (st != FA_OK) return st;
+    if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;  // grid y/z limit of the unfused kernels
+    const size_t need = workspace_bytes(B, H, N, elem);
+    if (!workspace || need == 0 || workspace_bytes_given < need || !aligned(workspace, kWsAlign))
+        return FA_ERR_WORKSPACE;
+    const Range rw = span(workspace, (int64_t)need);
+    const int64_t tbytes = (int64_t)B * H * N * d * elem;
+    for (Range r : {span(q, tbytes), span(k, tbytes), span(v, tbytes), span(o, tbytes),
+                    span(lse, (int64_t)B * H * N * 4), span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0)}) {
+        if (overlap(rw, r)) return FA_ERR_ALIAS;
+    }
+    const size_t rows = (size_t)B * H * N * (size_t)fa::unfused_ld(N);
+    float* S = static_cast<float*>(workspace);
+    void* P = static_cast<char*>(workspace) + round_up(rows * 4, kWsAlign);
+    return hip_status(fa::launch_unfused(bf16_path, q, k, v, o, lse, B, H, N, d, causal != 0, scale, kv_limit, S, P,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse, int B, int H,
+                      int N, int d, int causal, float scale, const int32_t* kv_limit, void* stream) {
+    fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, kv_limit, 2);
+    if (st != FA_OK) return st;
+    return hip_status(fa::launch_fused_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, kv_limit,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                     int d, int causal, float scale, const int32_t* kv_limit, void* stream) {
+    fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, kv_limit, 4);
+    if (st != FA_OK) return st;
+    return hip_status(fa::launch_fused_f32(q, k, v, o, lse, B, H, N, d, causal != 0, scale, kv_limit,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_unfused_workspace_bytes(int B, int H, int N, int elem_bytes) {
+    return workspace_bytes(B, H, N, elem_bytes);
+}
+
+fa_status fa_fwd_unfused_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+                              int B, int H, int N, int d, int causal, float scale, const int32_t* kv_limit,
+                              void* workspace, size_t workspace_bytes_given, void* stream) {
+    return unfused(true, q, k, v, o, lse, B, H, N, d, causal, scale, kv_limit, workspace, workspace_bytes_given,
+                   stream);
+}
+
+fa_status fa_fwd_unfused_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                             int N, int d, int causal, float scale, const int32_t* kv_limit, void* workspace,
+                             size_t workspace_bytes_given, void* stream) {
+    return unfused(false, q, k, v, o, lse, B, H, N, d, causal, scale, kv_limit, workspace, workspace_bytes_given,
+                   stream);
+}
+
+const char* fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "B, H or N out of range";
+        case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+        case FA_ERR_SCALE: return "scale must be finite and positive";
+        case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse and kv_limit 4-byte aligned";
+        case FA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case FA_ERR_ALIAS: return "an output overlaps an input, the other output or the workspace";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// fa_common.h -- types and small device helpers shared by the library's kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Cross-lane exchange with the lane 32 positions away (lanes i and i^32).
+__device__ __forceinline__ float swap_halves(float x) {
+    return __shfl_xor(x, 32, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+__device__ __forceinline__ int wave_max_i(int x) {
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+    for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+// Pack two fp32 values into bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 p;
+    p[0] = (bf16)lo;
+    p[1] = (bf16)hi;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Number of keys row `q` may attend to: keys j < limit are candidates, then the
+// causal condition j <= q is applied on top (limit <= q + 1).
+__device__ __forceinline__ int row_key_limit(int q, int N, bool causal, const int32_t* kv_limit_row) {
+    if (q >= N) return 0;
+    int lim = N;
+    if (kv_limit_row) {
+        int v = *kv_limit_row;
+        v = v < 0 ? 0 : v;
+        lim = v < lim ? v : lim;
+    }
+    if (causal && q + 1 < lim) lim = q + 1;
+    return lim;
+}
+
+}  // namespace fa

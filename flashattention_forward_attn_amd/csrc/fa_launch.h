@@ -1,0 +1,28 @@
+// fa_launch.h -- host-side launchers behind the C ABI (internal to libfa.so).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+hipError_t launch_fused_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                             int N, int d, bool causal, float scale, const int32_t* kv_limit,
+                             hipStream_t stream);
+
+hipError_t launch_fused_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                            int N, int d, bool causal, float scale, const int32_t* kv_limit,
+                            hipStream_t stream);
+
+// Row stride (elements) of the unfused path's S and P buffers: N rounded up to 64.
+inline int64_t unfused_ld(int N) { return ((int64_t)N + 63) / 64 * 64; }
+
+// Three launches: scores, masked row softmax, P V.  S is fp32 [B*H*N, ld];
+// P is bf16 (elem 2) or fp32 (elem 4) [B*H*N, ld].
+hipError_t launch_unfused(bool bf16_path, const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, bool causal, float scale, const int32_t* kv_limit,
+                          float* S, void* P, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,281 @@
+// fa_unfused.hip -- standard (unfused) attention forward: three kernels, with the
+// N x N score matrix S and probability matrix P making a round trip through
+// device memory.  This is the baseline the fused kernel replaces: "FlashAttention
+// 1–4: How IO-Awareness Reshaped the Attention Kernel", section "FlashAttention
+// (v1)", the figure contrasting standard attention (one kernel per step, S and P
+// out to HBM and back) with the fused kernel; "GPU 与 TPU：让硬件不再是黑魔法"
+// §11.1.  The softmax kernel is one row per workgroup with the row held in
+// registers, so S is read once and P written once ("GPU 与 Triton 入门" §2.2).
+//
+//   scores  : S[row, j] = scale * <q_row, k_j>            (fp32, every pair, no mask)
+//   softmax : P[row, j] = exp(S - max) / sum over valid j  (mask applied here), lse
+//   pv      : O[row, :] = sum_j P[row, j] v_j
+//
+// S and P rows have stride ld = N rounded up to 64; P is zero in [N, ld) so the
+// P V kernel reads whole 64-key tiles.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace unfused {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- scores (bf16)
+// Workgroup = 2 x 2 waves, each wave one 32 x 32 tile of S (query rows x keys):
+// C = A B with A = Q (row = query, k = dims), B = K^T (col = key, k = dims).
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                        float* __restrict__ S, int N, int64_t ld, float scale) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const size_t head = (size_t)blockIdx.z * N * D;
+    const int q0 = blockIdx.y * 64 + (w >> 1) * 32;
+    const int k0 = blockIdx.x * 64 + (w & 1) * 32;
+    const int qa = q0 + col, kb = k0 + col;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        bf16x8 a = bf16x8{}, bb = bf16x8{};
+        if (qa < N) a = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qa * D + 16 * kk + 8 * half);
+        if (kb < N) bb = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kb * D + 16 * kk + 8 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+    }
+    if (kb >= N) return;
+    float* Sh = S + (size_t)blockIdx.z * N * ld;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (q < N) Sh[(size_t)q * ld + kb] = acc[r] * scale;
+    }
+}
+
+// ---------------------------------------------------------------- scores (fp32)
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                                       float* __restrict__ S, int N, int64_t ld, float scale) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= (int64_t)N * N) return;
+    const int q = (int)(idx / N), j = (int)(idx % N);
+    const size_t head = (size_t)blockIdx.y * N * D;
+    const float* qr = Q + head + (size_t)q * D;
+    const float* kr = K + head + (size_t)j * D;
+    float acc = 0.f;
+    for (int c = 0; c < D; ++c) acc = fmaf(qr[c], kr[c], acc);
+    S[(size_t)blockIdx.y * N * ld + (size_t)q * ld + j] = acc * scale;
+}
+
+// ---------------------------------------------------------------- softmax rows
+__device__ __forceinline__ float block_reduce_max(float x, float* red) {
+    x = wave_max(x);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_reduce_sum(float x, float* red) {
+    x = wave_sum(x);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <typename PT>
+__device__ __forceinline__ PT to_p(float x);
+template <>
+__device__ __forceinline__ bf16 to_p<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ float to_p<float>(float x) { return x; }
+
+// One workgroup per row.  EPT > 0: the row lives in registers (EPT elements per
+// thread, EPT * 256 >= ld).  EPT == 0: long rows, three passes over S.
+template <typename PT, int EPT>
+__global__ __launch_bounds__(kThreads) void softmax_rows(const float* __restrict__ S, PT* __restrict__ P,
+                                                         float* __restrict__ LSE, int H, int N, int64_t ld,
+                                                         int causal, const int32_t* __restrict__ kv_limit) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const int i = (int)(row % N);
+    const int b = (int)(row / N) / H;
+    const int lim = row_key_limit(i, N, causal != 0, kv_limit ? kv_limit + (size_t)b * N + i : nullptr);
+    const float* srow = S + row * ld;
+    PT* prow = P + row * ld;
+    const int tid = threadIdx.x;
+
+    if constexpr (EPT > 0) {
+        float x[EPT];
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int j = tid + e * kThreads;
+            x[e] = j < N ? srow[j] : -INFINITY;
+            if (j >= lim) x[e] = -INFINITY;
+            m = fmaxf(m, x[e]);
+        }
+        m = block_reduce_max(m, red);
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int j = tid + e * kThreads;
+            x[e] = (j < lim) ? __expf(x[e] - m) : 0.f;
+            sum += x[e];
+        }
+        sum = block_reduce_sum(sum, red);
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int j = tid + e * kThreads;
+            if (j < ld) prow[j] = to_p<PT>(x[e] * inv);
+        }
+        if (tid == 0) LSE[row] = sum > 0.f ? m + __logf(sum) : -INFINITY;
+    } else {
+        float m = -INFINITY;
+        for (int j = tid; j < lim; j += kThreads) m = fmaxf(m, srow[j]);
+        m = block_reduce_max(m, red);
+        float sum = 0.f;
+        for (int j = tid; j < lim; j += kThreads) sum += __expf(srow[j] - m);
+        sum = block_reduce_sum(sum, red);
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+        for (int j = tid; j < ld; j += kThreads) prow[j] = to_p<PT>(j < lim ? __expf(srow[j] - m) * inv : 0.f);
+        if (tid == 0) LSE[row] = sum > 0.f ? m + __logf(sum) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- P V (bf16)
+// Workgroup = 4 waves x 32 query rows; keys in tiles of 64 with V^T staged in
+// LDS.  C = A B with A = P (row = query, k = keys), B = V (col = dim, k = keys).
+template <int D>
+__global__ __launch_bounds__(kThreads) void pv_bf16(const bf16* __restrict__ P, const bf16* __restrict__ V,
+                                                    bf16* __restrict__ O, int N, int64_t ld) {
+    constexpr int kBK = 64, kStride = kBK + 8;
+    __shared__ __attribute__((aligned(16))) bf16 Vt[D * kStride];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const size_t head = (size_t)blockIdx.y * N * D;
+    const int q0 = blockIdx.x * 128 + w * 32;
+    const int qa = q0 + col;
+    const bf16* prow = P + (size_t)blockIdx.y * N * ld + (size_t)(qa < N ? qa : 0) * ld;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+    for (int k0 = 0; k0 < N; k0 += kBK) {
+        __syncthreads();
+        for (int u = tid; u < 8 * (D / 4); u += kThreads) {
+            const int j = u & 7, c = u >> 3;
+            u32x2 r[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int key = k0 + 8 * j + s;
+                r[s] = key < N ? *reinterpret_cast<const u32x2*>(V + head + (size_t)key * D + 4 * c) : u32x2{0, 0};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u32x4 out;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t a = (e < 2) ? r[2 * p].x : r[2 * p].y;
+                    const uint32_t bq = (e < 2) ? r[2 * p + 1].x : r[2 * p + 1].y;
+                    out[p] = (e & 1) ? ((a >> 16) | (bq & 0xffff0000u)) : ((a & 0xffffu) | (bq << 16));
+                }
+                *reinterpret_cast<u32x4*>(Vt + (4 * c + e) * kStride + 8 * j) = out;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            bf16x8 a = bf16x8{};
+            if (qa < N) a = *reinterpret_cast<const bf16x8*>(prow + k0 + 16 * ks + 8 * half);
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    a, *reinterpret_cast<const bf16x8*>(Vt + (32 * t + col) * kStride + 16 * ks + 8 * half),
+                    acc[t], 0, 0, 0);
+        }
+    }
+    bf16* Oh = O + head;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (q < N) Oh[(size_t)q * D + 32 * t + col] = (bf16)acc[t][r];
+        }
+}
+
+// ---------------------------------------------------------------- P V (fp32)
+template <int D>
+__global__ __launch_bounds__(kThreads) void pv_f32(const float* __restrict__ P, const float* __restrict__ V,
+                                                   float* __restrict__ O, int N, int64_t ld) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= (int64_t)N * D) return;
+    const int q = (int)(idx / D), c = (int)(idx % D);
+    const size_t head = (size_t)blockIdx.y * N * D;
+    const float* prow = P + (size_t)blockIdx.y * N * ld + (size_t)q * ld;
+    float acc = 0.f;
+    for (int j = 0; j < N; ++j) acc = fmaf(prow[j], V[head + (size_t)j * D + c], acc);
+    O[head + (size_t)q * D + c] = acc;
+}
+
+template <typename PT>
+hipError_t launch_softmax(const float* S, PT* P, float* lse, int B, int H, int N, int64_t ld, bool causal,
+                          const int32_t* kv_limit, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)B * H * N));
+    const int c = causal ? 1 : 0;
+    if (ld <= 1 * kThreads)
+        hipLaunchKernelGGL((softmax_rows<PT, 1>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    else if (ld <= 4 * kThreads)
+        hipLaunchKernelGGL((softmax_rows<PT, 4>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    else if (ld <= 16 * kThreads)
+        hipLaunchKernelGGL((softmax_rows<PT, 16>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    else if (ld <= 64 * kThreads)
+        hipLaunchKernelGGL((softmax_rows<PT, 64>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    else
+        hipLaunchKernelGGL((softmax_rows<PT, 0>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    return hipGetLastError();
+}
+
+}  // namespace unfused
+
+hipError_t launch_unfused(bool bf16_path, const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, bool causal, float scale, const int32_t* kv_limit,
+                          float* S, void* P, hipStream_t stream) {
+    using namespace unfused;
+    const int64_t ld = unfused_ld(N);
+    const unsigned BH = (unsigned)((int64_t)B * H);
+    hipError_t err;
+    if (bf16_path) {
+        const dim3 g1((N + 63) / 64, (N + 63) / 64, BH);
+        if (d == 64)
+            hipLaunchKernelGGL((scores_bf16<64>), g1, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, S, N, ld, scale);
+        else
+            hipLaunchKernelGGL((scores_bf16<128>), g1, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, S, N, ld, scale);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_softmax<bf16>(S, (bf16*)P, lse, B, H, N, ld, causal, kv_limit, stream)) != hipSuccess) return err;
+        const dim3 g3((N + 127) / 128, BH);
+        if (d == 64)
+            hipLaunchKernelGGL((pv_bf16<64>), g3, dim3(kThreads), 0, stream, (const bf16*)P, (const bf16*)v, (bf16*)o, N, ld);
+        else
+            hipLaunchKernelGGL((pv_bf16<128>), g3, dim3(kThreads), 0, stream, (const bf16*)P, (const bf16*)v, (bf16*)o, N, ld);
+        return hipGetLastError();
+    }
+    const dim3 g1((unsigned)(((int64_t)N * N + kThreads - 1) / kThreads), BH);
+    if (d == 64)
+        hipLaunchKernelGGL((scores_f32<64>), g1, dim3(kThreads), 0, stream, (const float*)q, (const float*)k, S, N, ld, scale);
+    else
+        hipLaunchKernelGGL((scores_f32<128>), g1, dim3(kThreads), 0, stream, (const float*)q, (const float*)k, S, N, ld, scale);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_softmax<float>(S, (float*)P, lse, B, H, N, ld, causal, kv_limit, stream)) != hipSuccess) return err;
+    const dim3 g3((unsigned)(((int64_t)N * d + kThreads - 1) / kThreads), BH);
+    if (d == 64)
+        hipLaunchKernelGGL((pv_f32<64>), g3, dim3(kThreads), 0, stream, (const float*)P, (const float*)v, (float*)o, N, ld);
+    else
+        hipLaunchKernelGGL((pv_f32<128>), g3, dim3(kThreads), 0, stream, (const float*)P, (const float*)v, (float*)o, N, ld);
+    return hipGetLastError();
+}
+
+}  // namespace fa

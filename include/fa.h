@@ -1,0 +1,138 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library (libfa.so).
+ *
+ * The operation.  For every batch item b, head h and query row i:
+ *
+ *   o[b,h,i,:] = sum_j softmax_j( scale * <q[b,h,i,:], k[b,h,j,:]> + M[b,i,j] ) * v[b,h,j,:]
+ *   lse[b,h,i] = log sum_j exp( scale * <q[b,h,i,:], k[b,h,j,:]> + M[b,i,j] )   (natural log)
+ *
+ * with M = 0 where key j is valid for row i and -inf elsewhere; key j is valid
+ * when (kv_limit == NULL or j < kv_limit[b*N + i]) and (causal == 0 or j <= i).
+ * A row with no valid key gets o = 0 and lse = -inf.
+ *
+ *   - O = softmax(Q K^T / sqrt(d)) V, computed exactly: "FlashAttention 1–4: How
+ *     IO-Awareness Reshaped the Attention Kernel", section "Why attention is
+ *     memory-bound, not compute-bound", and its closing section on what all four
+ *     versions share.
+ *   - The additive mask M (-inf at future positions for causal attention) and the
+ *     [b, h, seq, d] layout: "谁偷走了 5090 的算力和显存", attention section.
+ *   - The per-row log-sum-exp L = m + log(l) kept for the backward pass:
+ *     "FlashAttention 1–4 ...", section "FlashAttention-2"; "GPU 与 TPU：让硬件不再是
+ *     黑魔法" §11.4.
+ *   - The fully masked row: "07 GPU、资源估算与 FlashAttention" §7.8 asks only that
+ *     -inf minus -inf never be computed; o = 0, lse = -inf is this library's reading
+ *     (the log of an empty sum).
+ *
+ * Layout.  q, k, v, o: contiguous [B, H, N, d] row-major, d fastest.  lse:
+ * contiguous [B, H, N] fp32.  kv_limit: NULL or contiguous [B, N] int32, values
+ * clamped to [0, N] (negative counts as 0).  Causal masking is top-left aligned
+ * with the diagonal included (query i sees keys 0..i).
+ *
+ * Supported shapes.  d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^31 elements per
+ * tensor (the unfused path also needs B*H <= 65535).  scale must be finite and
+ * positive (the pages use 1/sqrt(d)).
+ *
+ * Memory and ownership.  Every pointer is device memory owned by the caller.  The
+ * library allocates nothing, keeps no pointer after a call returns and has no
+ * mutable global state; calls are thread-safe.  o and lse must not overlap any
+ * input or each other.  q, k, v, o must be 16-byte aligned; lse and kv_limit 4-byte
+ * aligned.
+ *
+ * Streams and errors.  `stream` is a hipStream_t (NULL = the default stream).
+ * Every call validates its arguments on the host before touching the device; an
+ * invalid call returns an error code and launches nothing.  A valid call enqueues
+ * its kernels on `stream` and returns without synchronising: a fault inside a
+ * kernel surfaces at the caller's next synchronisation.  FA_ERR_HIP means a launch
+ * was rejected by the HIP runtime.  No C++ exception crosses this boundary.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t fa_bf16; /* raw bf16 bits (the upper half of an IEEE fp32) */
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL                              */
+    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 - 1 elements    */
+    FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                      */
+    FA_ERR_SCALE = 4,     /* scale is NaN, infinite, zero or negative                */
+    FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
+    FA_ERR_WORKSPACE = 6, /* unfused path: workspace NULL, too small or misaligned   */
+    FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch                */
+    FA_ERR_ALIAS = 8      /* an output overlaps an input, the other output or the workspace */
+} fa_status;
+
+/*
+ * Fused forward, bf16 inputs and output, fp32 accumulation and statistics.
+ * One kernel: Q tile in registers, K/V tiles streamed through LDS, both
+ * contractions on bf16 matrix cores, online softmax (running max, running sum,
+ * unnormalised accumulator rescaled per K/V tile, one normalisation at the end);
+ * the N x N score matrix never reaches device memory ("GPU 与 TPU：让硬件不再是
+ * 黑魔法" §11.2-§11.4; "FlashAttention 1–4 ...", sections "FlashAttention (v1)"
+ * and "FlashAttention-2").  The probabilities feeding P V are rounded to bf16
+ * (nearest-even) and the row sum l is taken over the same rounded values.
+ */
+fa_status fa_fwd_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
+                      fa_bf16 *o, float *lse,
+                      int B, int H, int N, int d, int causal, float scale,
+                      const int32_t *kv_limit, void *stream);
+
+/*
+ * Fused forward, fp32 inputs and output.  Same algorithm as fa_fwd_bf16 with the
+ * contractions on fp32 matrix cores and P kept in fp32.
+ */
+fa_status fa_fwd_f32(const float *q, const float *k, const float *v,
+                     float *o, float *lse,
+                     int B, int H, int N, int d, int causal, float scale,
+                     const int32_t *kv_limit, void *stream);
+
+/*
+ * Bytes of workspace the unfused path needs: S in fp32 plus P in the input
+ * precision (elem_bytes = 2 for bf16, 4 for fp32), each B*H*N rows of
+ * ld = (N rounded up to 64) elements, each part rounded up to 256 bytes.
+ * Returns 0 if the size would overflow size_t or an argument is out of range.
+ */
+size_t fa_unfused_workspace_bytes(int B, int H, int N, int elem_bytes);
+
+/*
+ * Unfused three-kernel forward, the standard attention the fused kernel replaces
+ * ("FlashAttention 1–4 ...", section "FlashAttention (v1)", the two-panel figure
+ * of standard attention: one kernel per step, S and P making a round trip
+ * through device memory):
+ *   kernel 1 writes S = scale * Q K^T (fp32) for every (query, key) pair;
+ *   kernel 2 reads S, applies the mask, runs a safe softmax one row per
+ *            workgroup and writes P (bf16, rounded to nearest-even) and lse;
+ *   kernel 3 reads P and V and writes O = P V.
+ * Same arguments and results as fa_fwd_bf16, plus a caller-owned device
+ * workspace of at least fa_unfused_workspace_bytes(B, H, N, 2) bytes, 256-byte
+ * aligned, not overlapping any input or output.
+ */
+fa_status fa_fwd_unfused_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
+                              fa_bf16 *o, float *lse,
+                              int B, int H, int N, int d, int causal, float scale,
+                              const int32_t *kv_limit,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Unfused three-kernel forward in fp32 (P stored in fp32); workspace of at least
+ * fa_unfused_workspace_bytes(B, H, N, 4) bytes. */
+fa_status fa_fwd_unfused_f32(const float *q, const float *k, const float *v,
+                             float *o, float *lse,
+                             int B, int H, int N, int d, int causal, float scale,
+                             const int32_t *kv_limit,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *fa_status_str(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,105 @@
+"""The C ABI library without a GPU: it loads, exports every function include/fa.h
+declares, and rejects invalid arguments on the host before any device call.
+
+Every call below is invalid in at least one argument, so nothing is ever
+launched: the fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from flashattention_forward_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# fake, well-aligned, non-overlapping device addresses (never dereferenced)
+Q, K, V, O, L, M, W = (0x10000000 * (i + 1) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"fa_fwd_bf16", "fa_fwd_f32", "fa_fwd_unfused_bf16", "fa_fwd_unfused_f32",
+            "fa_unfused_workspace_bytes", "fa_status_str"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.fa_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_str(99).decode() == "unknown status"
+
+
+def fwd(lib, name="fa_fwd_bf16", q=Q, k=K, v=V, o=O, l=L, B=2, H=3, N=100, d=128, causal=0, scale=0.125, m=None):
+    return getattr(lib, name)(q, k, v, o, l, B, H, N, d, causal, scale, m, None)
+
+
+@pytest.mark.parametrize("name", ["fa_fwd_bf16", "fa_fwd_f32"])
+def test_fused_validation(lib, name):
+    assert fwd(lib, name, q=None) == 1
+    assert fwd(lib, name, l=None) == 1
+    assert fwd(lib, name, B=0) == 2
+    assert fwd(lib, name, N=-5) == 2
+    assert fwd(lib, name, B=1 << 12, H=1 << 12, N=1 << 8, d=64) == 2  # 2^38 elements
+    assert fwd(lib, name, d=96) == 3
+    assert fwd(lib, name, d=256) == 3
+    assert fwd(lib, name, scale=float("nan")) == 4
+    assert fwd(lib, name, scale=float("inf")) == 4
+    assert fwd(lib, name, scale=0.0) == 4
+    assert fwd(lib, name, scale=-0.1) == 4
+    assert fwd(lib, name, q=Q + 8) == 5
+    assert fwd(lib, name, o=O + 2) == 5
+    assert fwd(lib, name, l=L + 2) == 5
+    assert fwd(lib, name, m=M + 1) == 5
+    assert fwd(lib, name, o=Q) == 8            # output over an input
+    assert fwd(lib, name, l=K + 64) == 8       # lse inside k
+    assert fwd(lib, name, l=O + 16) == 8       # lse inside o
+    assert fwd(lib, name, m=O + 1024) == 8     # kv_limit inside o
+
+
+def unfused(lib, name="fa_fwd_unfused_bf16", ws=W, ws_bytes=None, B=2, H=3, N=100, d=128, **kw):
+    elem = 2 if name.endswith("bf16") else 4
+    if ws_bytes is None:
+        ws_bytes = lib.fa_unfused_workspace_bytes(B, H, N, elem)
+    q, k, v, o, l = kw.get("q", Q), kw.get("k", K), kw.get("v", V), kw.get("o", O), kw.get("l", L)
+    return getattr(lib, name)(q, k, v, o, l, B, H, N, d, 0, kw.get("scale", 0.125), kw.get("m"), ws, ws_bytes,
+                              None)
+
+
+@pytest.mark.parametrize("name", ["fa_fwd_unfused_bf16", "fa_fwd_unfused_f32"])
+def test_unfused_validation(lib, name):
+    assert unfused(lib, name, q=None) == 1
+    assert unfused(lib, name, d=80) == 3
+    assert unfused(lib, name, scale=-1.0) == 4
+    assert unfused(lib, name, ws=None) == 6
+    assert unfused(lib, name, ws_bytes=100) == 6
+    assert unfused(lib, name, ws=W + 128) == 6        # 256-byte alignment
+    assert unfused(lib, name, ws=O) == 8              # workspace over the output
+    assert unfused(lib, name, B=300, H=300, N=1, d=64) == 2  # B*H beyond the grid limit
+    assert unfused(lib, name, o=K) == 8
+
+
+def test_workspace_bytes(lib):
+    f = lib.fa_unfused_workspace_bytes
+    # ld = N rounded up to 64; S fp32 + P (2 or 4 bytes), each part 256-aligned
+    assert f(1, 1, 64, 2) == 64 * 64 * 4 + 64 * 64 * 2
+    assert f(1, 1, 65, 2) == 65 * 128 * 4 + 65 * 128 * 2
+    assert f(1, 16, 16384, 2) == 16 * 16384 * 16384 * 6
+    assert f(2, 32, 4096, 4) == 2 * 32 * 4096 * 4096 * 8
+    assert f(1, 1, 3, 2) == 768 + 512  # S: 3*64*4 = 768; P: 3*64*2 = 384, rounded up to 512
+    assert f(0, 1, 1, 2) == 0 and f(1, 1, 1, 3) == 0

@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element.
+
+  - an odd-size sweep: N from 1 to 257 across tile edges, d in {64, 128},
+    causal on and off, four key-limit patterns, fused and unfused;
+  - the five workloads at full size: full oracle where it finishes in seconds,
+    otherwise sampled rows (first and last rows, tile edges, the diagonal, the
+    masked query block) plus properties over every row;
+  - determinism, key permutation, fully masked rows and the causal first row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_forward_attn_amd import inputs
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+SWEEP_N = [1, 2, 3, 5, 16, 17, 63, 64, 65, 127, 128, 129, 200, 255, 257]
+MASKS = [None, "random", "some_zero", "zeros"]
+
+
+def _limits(kind, B, N, seed):
+    return None if kind is None else inputs.random_kv_limit(B, N, seed, kind)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SWEEP_N)
+def test_sweep_fused_bf16(N, causal, d):
+    w = inputs.custom(f"sweep_{N}_{d}", "bf16", 2, 3, N, d, causal, seed=N * 7 + d)
+    x = inputs.generate(w)
+    for mi, kind in enumerate(MASKS):
+        lim = _limits(kind, 2, N, seed=1000 + N + mi)
+        o, lse = gh.run(x, kv_limit_override=lim) if lim is not None else gh.run(x)
+        ro, rl = oracle.attention(x.q, x.k, x.v, causal, w.scale, lim, nthreads=gh.oracle_threads())
+        gh.compare("bf16", o, lse, ro, rl, f"fused bf16 N={N} d={d} causal={causal} mask={kind}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 257])
+def test_sweep_fused_f32(N, causal, d):
+    w = inputs.custom(f"sweep32_{N}_{d}", "f32", 2, 2, N, d, causal, seed=N * 11 + d)
+    x = inputs.generate(w)
+    for mi, kind in enumerate(MASKS):
+        lim = _limits(kind, 2, N, seed=2000 + N + mi)
+        o, lse = gh.run(x, kv_limit_override=lim) if lim is not None else gh.run(x)
+        ro, rl = oracle.attention(x.q, x.k, x.v, causal, w.scale, lim, nthreads=gh.oracle_threads())
+        gh.compare("f32", o, lse, ro, rl, f"fused f32 N={N} d={d} causal={causal} mask={kind}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 65, 200, 257])
+def test_sweep_unfused(N, causal, d, dtype):
+    w = inputs.custom(f"sweepu_{N}_{d}", dtype, 2, 2, N, d, causal, seed=N * 13 + d)
+    x = inputs.generate(w)
+    for mi, kind in enumerate(MASKS):
+        lim = _limits(kind, 2, N, seed=3000 + N + mi)
+        o, lse = gh.run(x, unfused=True, kv_limit_override=lim) if lim is not None else gh.run(x, unfused=True)
+        ro, rl = oracle.attention(x.q, x.k, x.v, causal, w.scale, lim, nthreads=gh.oracle_threads())
+        gh.compare(dtype, o, lse, ro, rl, f"unfused {dtype} N={N} d={d} causal={causal} mask={kind}")
+
+
+def _sample_rows(w: inputs.Workload, x: inputs.Inputs, count: int, seed: int) -> np.ndarray:
+    """Flat row ids (b*H + h)*N + i: random rows plus edges and special rows."""
+    rng = np.random.default_rng(seed)
+    B, H, N = w.B, w.H, w.N
+    special_i = sorted({0, 1, 31, 32, 63, 64, 65, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64,
+                        N - 2, N - 1} & set(range(N)))
+    ids = set(rng.integers(0, B * H * N, size=count).tolist())
+    for b in range(B):
+        h = int(rng.integers(0, H))
+        for i in special_i:
+            ids.add((b * H + h) * N + i)
+    if x.masked_batch is not None:
+        b = x.masked_batch
+        for i in range(x.masked_q0, min(x.masked_q0 + inputs.MASKED_QUERY_BLOCK, N), 9):
+            ids.add((b * H + int(rng.integers(0, H))) * N + i)
+        for b in range(B):  # rows around each batch item's valid length
+            L = int(x.lengths[b])
+            for i in (L - 1, L, L + 1):
+                if 0 <= i < N:
+                    ids.add((b * H) * N + i)
+    return np.array(sorted(ids), np.int64)
+
+
+@pytest.mark.parametrize("name", ["f32_b1h1n256d64", "bf16_b4h16n2048d64"])
+def test_workload_full_oracle(name):
+    w = inputs.WORKLOADS[name]
+    x = inputs.generate(w)
+    ro, rl = oracle.attention(x.q, x.k, x.v, w.causal, w.scale, x.kv_limit, nthreads=gh.oracle_threads())
+    for unfused in (False, True):
+        o, lse = gh.run(x, unfused=unfused)
+        stats = gh.compare(w.dtype, o, lse, ro, rl, f"{name} unfused={unfused}")
+        print(name, "unfused" if unfused else "fused", stats)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_b2h32n4096d128", "bf16_causal_b1h16n16384d128",
+                                  "bf16_keypad_b8h32n1024d128"])
+def test_workload_sampled_rows(name):
+    w = inputs.WORKLOADS[name]
+    x = inputs.generate(w)
+    ids = _sample_rows(w, x, count=1500, seed=17)
+    ro, rl = oracle.attention_rows(x.q, x.k, x.v, ids, w.causal, w.scale, x.kv_limit,
+                                   nthreads=gh.oracle_threads())
+    for unfused in (False, True):
+        o, lse = gh.run(x, unfused=unfused)
+        of, lf = o.reshape(-1, w.d), lse.reshape(-1)
+        stats = gh.compare("bf16", of[ids], lf[ids], ro, rl, f"{name} unfused={unfused} (sampled)")
+        print(name, "unfused" if unfused else "fused", len(ids), "rows", stats)
+        # every row: finite where a key is valid, exact zeros / -inf where none is
+        assert np.all(np.isfinite(o))
+        if x.kv_limit is not None:
+            empty = x.kv_limit == 0  # [B, N]; the key-padding workload is not causal
+            assert np.all(np.isneginf(lse[np.broadcast_to(empty[:, None, :], lse.shape)]))
+            assert np.all(o[np.broadcast_to(empty[:, None, :], lse.shape)] == 0.0)
+            assert np.all(np.isfinite(lse[np.broadcast_to(~empty[:, None, :], lse.shape)]))
+        else:
+            assert np.all(np.isfinite(lse))
+
+
+def test_deterministic():
+    w = inputs.custom("det", "bf16", 2, 4, 1000, 128, True, seed=5)
+    x = inputs.generate(w)
+    o1, l1 = gh.run(x)
+    o2, l2 = gh.run(x)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_key_permutation_invariance():
+    w = inputs.custom("perm", "bf16", 1, 4, 777, 64, False, seed=6)
+    x = inputs.generate(w)
+    perm = np.random.default_rng(7).permutation(w.N)
+    o1, l1 = gh.run(x)
+    xp = inputs.Inputs(w, x.q, x.k[:, :, perm], x.v[:, :, perm], None,
+                       x.q_bits, np.ascontiguousarray(x.k_bits[:, :, perm]), np.ascontiguousarray(x.v_bits[:, :, perm]))
+    o2, l2 = gh.run(xp)
+    assert np.abs(o1 - o2).max() <= gh.BF16_MAX_ABS
+    assert np.abs(o1 - o2).mean() <= gh.BF16_MEAN_ABS
+    assert np.abs(l1 - l2).max() <= 1e-3
+
+
+def test_causal_first_row_is_first_value():
+    w = inputs.custom("row0", "bf16", 2, 3, 300, 128, True, seed=8)
+    x = inputs.generate(w)
+    o, lse = gh.run(x)
+    np.testing.assert_array_equal(o[:, :, 0], x.v[:, :, 0].astype(np.float64))
+    s00 = (x.q[:, :, 0].astype(np.float64) * x.k[:, :, 0]).sum(-1) * w.scale
+    np.testing.assert_allclose(lse[:, :, 0], s00, atol=1e-4)
+
+
+def test_all_rows_masked():
+    w = inputs.custom("allmask", "bf16", 2, 2, 190, 64, False, seed=9)
+    x = inputs.generate(w)
+    lim = np.zeros((2, 190), np.int32)
+    for unfused in (False, True):
+        o, lse = gh.run(x, unfused=unfused, kv_limit_override=lim)
+        assert np.all(o == 0.0) and np.all(np.isneginf(lse))
