@@ -117,15 +117,17 @@ def cpu_baseline(x, target_seconds: float):
     threads = host_threads()
     rows_total = w.B * w.H * w.N
     flops_per_row = w.flops() / rows_total
-    n_cal = min(rows_total, 4 * threads)
+    # the oracle takes fp64; widen once so the timed calls do no conversion
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (x.q, x.k, x.v))
+    n_cal = min(rows_total, 64 * threads)
     ids = np.linspace(0, rows_total - 1, n_cal).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.attention_rows(x.q, x.k, x.v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
+    oracle.attention_rows(q, k, v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
     cal = time.perf_counter() - t0
     n = int(min(rows_total, max(n_cal, n_cal * target_seconds / max(cal, 1e-6))))
     ids = np.unique(np.linspace(0, rows_total - 1, n).astype(np.int64))
     t0 = time.perf_counter()
-    oracle.attention_rows(x.q, x.k, x.v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
+    oracle.attention_rows(q, k, v, ids, w.causal, w.scale, x.kv_limit, nthreads=threads)
     dt = time.perf_counter() - t0
     return {
         "value": ids.size * flops_per_row / dt / 1e12,
@@ -150,11 +152,14 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
+                         "its FETCH_SIZE/WRITE_SIZE calibrate the traffic counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the forward pass shards over (batch, head) with no communication; see DESIGN.md)",
+              "(the forward pass shards over (batch, head) with no communication between GPUs)",
               file=sys.stderr)
         return 2
 
@@ -164,6 +169,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+        return 0
     binding.load()
 
     w = inputs.WORKLOADS[args.workload]

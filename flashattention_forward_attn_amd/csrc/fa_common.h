@@ -18,9 +18,30 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Cross-lane exchange with the lane 32 positions away (lanes i and i^32).
-__device__ __forceinline__ float swap_halves(float x) {
-    return __shfl_xor(x, 32, kWave);
+// Combine the two lane halves (lanes i and i ^ 32) with one v_permlane32_swap:
+// afterwards {a, b} of every lane hold x from lane i % 32 and lane i % 32 + 32.
+__device__ __forceinline__ float halves_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Make the compiler treat v as produced here: values loaded once before a loop
+// then carry no memory-counter dependency into it.
+template <typename T>
+__device__ __forceinline__ void launder(T& v) {
+    asm volatile("" : "+v"(v));
 }
 
 __device__ __forceinline__ float wave_max(float x) {

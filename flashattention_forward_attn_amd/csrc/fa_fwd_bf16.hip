@@ -79,23 +79,25 @@ struct Prefetch {
     u32x2 v[8];
 };
 
+// Global -> registers for K/V tile starting at key kv0.  Rows past N read as
+// zeros through the buffer range check, so no load is predicated.
 template <int D>
-__device__ __forceinline__ void load_tile(Prefetch<D>& pf, const bf16* __restrict__ Kh,
-                                          const bf16* __restrict__ Vh, int kv0, int N, int tid) {
+__device__ __forceinline__ void load_tile(Prefetch<D>& pf, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          int kv0, int tid) {
     using T = Tile<D>;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
         const int ci = tid + i * kThreads;
         const int row = ci / (D / 8), col8 = ci % (D / 8);
-        const int key = kv0 + row;
-        pf.k[i] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
+        const uint32_t off = ((uint32_t)(kv0 + row) * D + col8 * 8) * 2u;
+        pf.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
     }
     if (tid < T::vUnits) {
         const int j = tid & 7, c = tid >> 3;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int key = kv0 + group_key(j, s);
-            pf.v[s] = key < N ? *reinterpret_cast<const u32x2*>(Vh + (size_t)key * D + 4 * c) : u32x2{0, 0};
+            const uint32_t off = ((uint32_t)(kv0 + group_key(j, s)) * D + 4 * c) * 2u;
+            pf.v[s] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0));
         }
     }
 }
@@ -148,8 +150,9 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows of the head first
     const int b = bh / H;
     const size_t head = (size_t)bh * N * D;
-    const bf16* Kh = K + head;
-    const bf16* Vh = V + head;
+    const uint32_t head_bytes = (uint32_t)N * D * 2u;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V + head, head_bytes);
 
     const int q0 = qb * kBQ;
     const int qrow = q0 + w * kQPW + col;
@@ -166,6 +169,8 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             qf[kk] = bf16x8{};
     }
     __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) launder(qf[kk]);
     const int kv_end = max(max(block_max[0], block_max[1]), max(block_max[2], block_max[3]));
     const int ntiles = (kv_end + kBK - 1) / kBK;
 
@@ -176,14 +181,14 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
     Prefetch<D> pf;
     if (ntiles > 0) {
-        load_tile<D>(pf, Kh, Vh, 0, N, tid);
+        load_tile<D>(pf, krs, vrs, 0, tid);
         store_tile<D>(pf, smem, tid);
     }
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const bool more = t + 1 < ntiles;
-        if (more) load_tile<D>(pf, Kh, Vh, (t + 1) * kBK, N, tid);
+        if (more) load_tile<D>(pf, krs, vrs, (t + 1) * kBK, tid);
         const bf16* Ks = smem + (t & 1) * T::stageElems;
         const bf16* Vts = Ks + T::kElems;
         const int kv0 = t * kBK;
@@ -214,7 +219,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-            mx = fmaxf(mx, swap_halves(mx));
+            mx = halves_max(mx);
             const float mt = mx * c;  // this tile's row max, log2 units
             if (__any(mt > m_ref + kStaleMax)) {
                 const float m_new = fmaxf(m_ref, mt);
@@ -259,7 +264,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     }
 
     // Epilogue: one division per row; each lane half summed its own keys.
-    const float l_tot = l_sum + swap_halves(l_sum);
+    const float l_tot = halves_sum(l_sum);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < N) {
         bf16* orow = O + head + (size_t)qrow * D;

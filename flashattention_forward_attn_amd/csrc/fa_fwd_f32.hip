@@ -100,7 +100,7 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, swap_halves(mx));
+        mx = halves_max(mx);
         const float mt = mx * c;
         if (__any(mt > m_ref)) {
             const float m_new = fmaxf(m_ref, mt);
@@ -129,7 +129,7 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
             }
     }
 
-    const float l_tot = l_sum + swap_halves(l_sum);
+    const float l_tot = halves_sum(l_sum);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < N) {
         float* orow = O + head + (size_t)qrow * D;
