@@ -10,9 +10,10 @@
 // never reach device memory.
 //
 // gfx950 design (not the pages' A100/H100 tiling):
-//   * 4 waves x 32 query rows = 128 rows per workgroup (split-Q: each wave owns
-//     its rows outright, no cross-wave reduction, "FlashAttention 1–4 ...",
-//     section "FlashAttention-2", warp partitioning).
+//   * 8 waves x 32 query rows = 256 rows per workgroup, two waves per SIMD
+//     (split-Q: each wave owns its rows outright, no cross-wave reduction,
+//     "FlashAttention 1–4 ...", section "FlashAttention-2", warp partitioning).
+//     Every K/V tile staged in LDS serves 256 queries.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     lane l then holds query (l & 31) and 16 of the 32 keys of a 32-key slab,
 //     the other 16 sitting in lane l ^ 32.  Row max and row sum are in-lane
@@ -36,18 +37,21 @@
 //     ragged tail and key padding).  A row that has seen no valid key keeps a
 //     finite exponent reference, so -inf - (-inf) is never formed
 //     ("07 GPU、资源估算与 FlashAttention" §7.8).
-//   * Workgroup order: all query blocks of a head run on one XCD (shared L2
-//     for that head's K/V), and causal heads start with their longest rows.
+//   * Workgroup order: query-block major, (batch, head) minor, and for causal
+//     attention the longest rows first over the whole grid (longest-processing-
+//     time-first, "FlashAttention 1–4 ...", section "FlashAttention-4").  With
+//     round-robin dispatch over the 8 XCDs, each XCD then sees a fixed subset
+//     of heads, and concurrently running workgroups read different heads.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace fused_bf16 {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;  // 256
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = 32;                  // query rows per wave
-constexpr int kBQ = kWaves * kQPW;        // 128 query rows per workgroup
+constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
 constexpr int kBK = 64;                   // keys per K/V tile
 constexpr int kPad = 8;                   // bf16 padding per LDS row (bank spread)
 constexpr float kStaleMax = 8.0f;         // log2 units
@@ -93,7 +97,7 @@ __device__ __forceinline__ void load_tile(Prefetch<D>& pf, __amdgpu_buffer_rsrc_
         pf.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
     }
     if (tid < T::vUnits) {
-        const int j = tid & 7, c = tid >> 3;
+        const int j = tid % (kBK / 8), c = tid / (kBK / 8);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const uint32_t off = ((uint32_t)(kv0 + group_key(j, s)) * D + 4 * c) * 2u;
@@ -112,7 +116,7 @@ __device__ __forceinline__ void store_tile(const Prefetch<D>& pf, bf16* __restri
         *reinterpret_cast<u32x4*>(stage + row * T::kStride + col8 * 8) = pf.k[i];
     }
     if (tid < T::vUnits) {
-        const int j = tid & 7, c = tid >> 3;
+        const int j = tid % (kBK / 8), c = tid / (kBK / 8);
         bf16* vt = stage + T::kElems + (4 * c) * T::vStride + 8 * j;
         // 8 keys x 4 dims in registers -> 4 dims x 8 keys in LDS
 #pragma unroll
@@ -141,13 +145,11 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
 
-    // Workgroups are dealt round-robin over the 8 XCDs; remap so consecutive
-    // query blocks of one head land on the same XCD.
     const int G = gridDim.x, bid = blockIdx.x;
-    const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;  // longest rows of the head first
+    const int BHn = G / nqb;
+    int qb = bid / BHn;
+    const int bh = bid - qb * BHn;
+    if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first over the whole grid
     const int b = bh / H;
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -171,7 +173,9 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) launder(qf[kk]);
-    const int kv_end = max(max(block_max[0], block_max[1]), max(block_max[2], block_max[3]));
+    int kv_end = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
     const int ntiles = (kv_end + kBK - 1) / kBK;
 
     f32x16 oacc[D / 32];
