@@ -152,6 +152,8 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
+    ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
+                    help="time the fused kernel (default) or the unfused three-kernel baseline as the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
                          "its FETCH_SIZE/WRITE_SIZE calibrate the traffic counters")
@@ -182,14 +184,15 @@ def main() -> int:
 
     w = inputs.WORKLOADS[args.workload]
     x = inputs.generate(w)
-    ms = measure_fused(torch, binding, x, args.steps, args.warmup)
+    measure = measure_fused if args.path == "fused" else measure_unfused
+    ms = measure(torch, binding, x, args.steps, args.warmup)
     tflops = w.flops() / (ms * 1e-3) / 1e12
 
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
             t = json.load(f).get(w.name)
-        if t and t.get("kernel_source_sha256") == _kernel_digest():
+        if t and t.get("path", "fused") == args.path and t.get("kernel_source_sha256") == _kernel_digest():
             traffic = t.get("bytes_per_launch")
 
     line = {
@@ -206,11 +209,15 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "scale": "1/sqrt(d)", "flops_per_step": w.flops(), "parallelism": "single GPU"},
+                   "scale": "1/sqrt(d)", "flops_per_step": w.flops(), "path": args.path,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
-    if not args.no_extras:
+    if args.path == "unfused":
+        line["roofline"]["bound"] = "hbm"
+        line["roofline"]["note"] = "three kernels per step; see unfused bytes in the profile summary"
+    if not args.no_extras and args.path == "fused":
         ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
         line["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
                            "fused_speedup": round(ums / ms, 2)}
