@@ -26,6 +26,7 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 constexpr size_t kWsAlign = 256;
+constexpr int kUnfusedMaxN = 32768;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -71,6 +72,7 @@ fa_status unfused(bool bf16_path, const void* q, const void* k, const void* v, v
     fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, kv_limit, elem);
     if (st != FA_OK) return st;
     if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;  // grid y/z limit of the unfused kernels
+    if (N > kUnfusedMaxN) return FA_ERR_SHAPE;         // 32-bit offsets into one head's P
     const size_t need = workspace_bytes(B, H, N, elem);
     if (!workspace || need == 0 || workspace_bytes_given < need || !aligned(workspace, kWsAlign))
         return FA_ERR_WORKSPACE;

@@ -198,17 +198,18 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const int kv0 = t * kBK;
 
         if (kv0 < wmax) {
-            // S^T = K Q^T for two 32-key slabs
+            // S^T = K Q^T for two 32-key slabs; the two accumulator chains alternate
             f32x16 s[2];
+            s[0] = f32x16{};
+            s[1] = f32x16{};
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                s[sub] = f32x16{};
-                const bf16* kp = Ks + (sub * 32 + col) * T::kStride + 8 * half;
+            for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
+                for (int sub = 0; sub < 2; ++sub) {
+                    const bf16* kp = Ks + (sub * 32 + col) * T::kStride + 8 * half;
                     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         *reinterpret_cast<const bf16x8*>(kp + 16 * kk), qf[kk], s[sub], 0, 0, 0);
-            }
+                }
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
@@ -252,16 +253,16 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                     l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
                 }
             }
-            // O^T += V^T P^T
+            // O^T += V^T P^T; the D/32 accumulator chains alternate
 #pragma unroll
-            for (int d32 = 0; d32 < D / 32; ++d32) {
-                const bf16* vp = Vts + (32 * d32 + col) * T::vStride + 8 * half;
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int d32 = 0; d32 < D / 32; ++d32) {
+                    const bf16* vp = Vts + (32 * d32 + col) * T::vStride + 8 * half;
                     oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         *reinterpret_cast<const bf16x8*>(vp + 16 * ks), __builtin_bit_cast(bf16x8, pk[ks]),
                         oacc[d32], 0, 0, 0);
-            }
+                }
         }
         if (more) store_tile<D>(pf, smem + ((t + 1) & 1) * T::stageElems, tid);
         __syncthreads();

@@ -13,6 +13,8 @@
 //
 // S and P rows have stride ld = N rounded up to 64; P is zero in [N, ld) so the
 // P V kernel reads whole 64-key tiles.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -22,31 +24,58 @@ namespace unfused {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- scores (bf16)
-// Workgroup = 2 x 2 waves, each wave one 32 x 32 tile of S (query rows x keys):
-// C = A B with A = Q (row = query, k = dims), B = K^T (col = key, k = dims).
+// Workgroup = 4 waves, a 128 (query) x 128 (key) tile of S.  The K tile is
+// staged in LDS once per workgroup; each wave keeps its 32 query rows' Q
+// fragments in registers and computes 4 slabs of 32 keys with C = A B,
+// A = Q (row = query, k = dims), B = K^T (col = key, k = dims).  S is written
+// with streaming stores: it is far larger than any cache.
+constexpr int kScoreTile = 128;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void scores_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                         float* __restrict__ S, int N, int64_t ld, float scale) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int kStride = D + 8;
+    __shared__ __attribute__((aligned(16))) bf16 Ks[kScoreTile * kStride];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const size_t head = (size_t)blockIdx.z * N * D;
-    const int q0 = blockIdx.y * 64 + (w >> 1) * 32;
-    const int k0 = blockIdx.x * 64 + (w & 1) * 32;
-    const int qa = q0 + col, kb = k0 + col;
-    f32x16 acc = f32x16{};
+    const int q0 = blockIdx.y * kScoreTile + w * 32;
+    const int k0 = blockIdx.x * kScoreTile;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + head, (uint32_t)N * D * 2u);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8 a = bf16x8{}, bb = bf16x8{};
-        if (qa < N) a = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qa * D + 16 * kk + 8 * half);
-        if (kb < N) bb = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kb * D + 16 * kk + 8 * half);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+    for (int i = 0; i < kScoreTile * D / 8 / kThreads; ++i) {
+        const int ci = tid + i * kThreads;
+        const int row = ci / (D / 8), c8 = ci % (D / 8);
+        const uint32_t off = ((uint32_t)(k0 + row) * D + 8 * c8) * 2u;  // rows past N read as zeros
+        *reinterpret_cast<u32x4*>(Ks + row * kStride + 8 * c8) =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
     }
-    if (kb >= N) return;
+    const int qa = q0 + col;
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = qa < N ? *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qa * D + 16 * kk + 8 * half) : bf16x8{};
+    __syncthreads();
+    f32x16 acc[kScoreTile / 32];
+#pragma unroll
+    for (int sub = 0; sub < kScoreTile / 32; ++sub) acc[sub] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int sub = 0; sub < kScoreTile / 32; ++sub)
+            acc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                qf[kk], *reinterpret_cast<const bf16x8*>(Ks + (sub * 32 + col) * kStride + 16 * kk + 8 * half),
+                acc[sub], 0, 0, 0);
     float* Sh = S + (size_t)blockIdx.z * N * ld;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (q < N) Sh[(size_t)q * ld + kb] = acc[r] * scale;
+    for (int sub = 0; sub < kScoreTile / 32; ++sub) {
+        const int key = k0 + sub * 32 + col;
+        if (key >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (q < N) __builtin_nontemporal_store(acc[sub][r] * scale, Sh + (size_t)q * ld + key);
+        }
     }
 }
 
@@ -146,56 +175,81 @@ __global__ __launch_bounds__(kThreads) void softmax_rows(const float* __restrict
 }
 
 // ---------------------------------------------------------------- P V (bf16)
-// Workgroup = 4 waves x 32 query rows; keys in tiles of 64 with V^T staged in
-// LDS.  C = A B with A = P (row = query, k = keys), B = V (col = dim, k = keys).
+// Workgroup = 4 waves x 32 query rows; keys in chunks of 64.  While chunk k is
+// multiplied, chunk k+1's P fragments (registers) and V rows (registers, then
+// LDS transposed to [dim][key]) are in flight.  C = A B with A = P (row =
+// query, k = keys), B = V (col = dim, k = keys).
 template <int D>
 __global__ __launch_bounds__(kThreads) void pv_bf16(const bf16* __restrict__ P, const bf16* __restrict__ V,
                                                     bf16* __restrict__ O, int N, int64_t ld) {
-    constexpr int kBK = 64, kStride = kBK + 8;
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * kStride];
+    constexpr int kBK = 64, kStride = kBK + 8, kUnits = (kBK / 8) * (D / 4);
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * kStride];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const size_t head = (size_t)blockIdx.y * N * D;
     const int q0 = blockIdx.x * 128 + w * 32;
     const int qa = q0 + col;
-    const bf16* prow = P + (size_t)blockIdx.y * N * ld + (size_t)(qa < N ? qa : 0) * ld;
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    // rows past N (and keys past N, which P holds as zeros up to ld) read as zeros
+    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(P + (size_t)blockIdx.y * N * ld, (uint32_t)((uint64_t)N * ld * 2u));
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V + head, (uint32_t)N * D * 2u);
+    const int j = tid & 7, c = tid >> 3;  // V unit: 8 consecutive keys x 4 dims
 
-    for (int k0 = 0; k0 < N; k0 += kBK) {
-        __syncthreads();
-        for (int u = tid; u < 8 * (D / 4); u += kThreads) {
-            const int j = u & 7, c = u >> 3;
-            u32x2 r[8];
+    bf16x8 pa[2][kBK / 16];
+    u32x2 vr[8];
+    // buffer indices are compile-time constants so pa stays in registers
+    auto load = [&](auto buf_c, int k0) {
+        constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int key = k0 + 8 * j + s;
-                r[s] = key < N ? *reinterpret_cast<const u32x2*>(V + head + (size_t)key * D + 4 * c) : u32x2{0, 0};
-            }
+        for (int ks = 0; ks < kBK / 16; ++ks)
+            pa[buf][ks] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(prs, ((uint32_t)qa * (uint32_t)ld + k0 + 16 * ks + 8 * half) * 2u, 0, 0));
+        if (kUnits == kThreads || tid < kUnits) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                vr[s] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, ((uint32_t)(k0 + 8 * j + s) * D + 4 * c) * 2u, 0, 0));
+        }
+    };
+    auto stage = [&](auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
+        if (kUnits == kThreads || tid < kUnits) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 u32x4 out;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const uint32_t a = (e < 2) ? r[2 * p].x : r[2 * p].y;
-                    const uint32_t bq = (e < 2) ? r[2 * p + 1].x : r[2 * p + 1].y;
+                    const uint32_t a = (e < 2) ? vr[2 * p].x : vr[2 * p].y;
+                    const uint32_t bq = (e < 2) ? vr[2 * p + 1].x : vr[2 * p + 1].y;
                     out[p] = (e & 1) ? ((a >> 16) | (bq & 0xffff0000u)) : ((a & 0xffffu) | (bq << 16));
                 }
-                *reinterpret_cast<u32x4*>(Vt + (4 * c + e) * kStride + 8 * j) = out;
+                *reinterpret_cast<u32x4*>(&Vt[buf][(4 * c + e) * kStride + 8 * j]) = out;
             }
         }
-        __syncthreads();
+    };
+    f32x16 acc[D / 32];
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            bf16x8 a = bf16x8{};
-            if (qa < N) a = *reinterpret_cast<const bf16x8*>(prow + k0 + 16 * ks + 8 * half);
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    const int nchunks = (N + kBK - 1) / kBK;
+    auto chunk = [&](auto cur_c, int kc) {
+        constexpr int cur = decltype(cur_c)::value;
+        const bool more = kc + 1 < nchunks;
+        if (more) load(std::integral_constant<int, cur ^ 1>{}, (kc + 1) * kBK);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
             for (int t = 0; t < D / 32; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a, *reinterpret_cast<const bf16x8*>(Vt + (32 * t + col) * kStride + 16 * ks + 8 * half),
+                    pa[cur][ks], *reinterpret_cast<const bf16x8*>(&Vt[cur][(32 * t + col) * kStride + 16 * ks + 8 * half]),
                     acc[t], 0, 0, 0);
-        }
+        if (more) stage(std::integral_constant<int, cur ^ 1>{});
+        __syncthreads();
+    };
+    load(std::integral_constant<int, 0>{}, 0);
+    stage(std::integral_constant<int, 0>{});
+    __syncthreads();
+    for (int kc = 0; kc < nchunks; kc += 2) {
+        chunk(std::integral_constant<int, 0>{}, kc);
+        if (kc + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, kc + 1);
     }
     bf16* Oh = O + head;
 #pragma unroll
@@ -249,7 +303,7 @@ hipError_t launch_unfused(bool bf16_path, const void* q, const void* k, const vo
     const unsigned BH = (unsigned)((int64_t)B * H);
     hipError_t err;
     if (bf16_path) {
-        const dim3 g1((N + 63) / 64, (N + 63) / 64, BH);
+        const dim3 g1((N + kScoreTile - 1) / kScoreTile, (N + kScoreTile - 1) / kScoreTile, BH);
         if (d == 64)
             hipLaunchKernelGGL((scores_bf16<64>), g1, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, S, N, ld, scale);
         else

@@ -29,7 +29,7 @@
  * with the diagonal included (query i sees keys 0..i).
  *
  * Supported shapes.  d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^31 elements per
- * tensor (the unfused path also needs B*H <= 65535).  scale must be finite and
+ * tensor (the unfused path also needs B*H <= 65535 and N <= 32768).  scale must be finite and
  * positive (the pages use 1/sqrt(d)).
  *
  * Memory and ownership.  Every pointer is device memory owned by the caller.  The

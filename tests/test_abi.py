@@ -92,6 +92,7 @@ def test_unfused_validation(lib, name):
     assert unfused(lib, name, ws=O) == 8              # workspace over the output
     assert unfused(lib, name, B=300, H=300, N=1, d=64) == 2  # B*H beyond the grid limit
     assert unfused(lib, name, o=K) == 8
+    assert unfused(lib, name, B=1, H=1, N=32769, d=64) == 2  # N beyond the unfused limit
 
 
 def test_workspace_bytes(lib):
