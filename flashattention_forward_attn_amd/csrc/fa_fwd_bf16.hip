@@ -19,18 +19,23 @@
 //     the other 16 sitting in lane l ^ 32.  Row max and row sum are in-lane
 //     reductions plus one exchange between the two lane halves.
 //   * O^T = V^T P^T: the exponentiated score accumulators, packed to bf16, are
-//     the B operand of the second contraction straight from registers.  V is
-//     written into LDS transposed ([dim][key]) with keys permuted so that each
-//     lane's 8 keys of a k-step are contiguous (one 16-byte LDS read); the
-//     permutation is the accumulator row order of the first contraction.
+//     the B operand of the second contraction straight from registers.  V stays
+//     row-major in LDS; its A operand is read with ds_read_b64_tr_b16, which
+//     transposes 4x4 blocks of 16-bit values across lanes, and the per-lane source
+//     addresses pick the keys in the accumulator row order of the first
+//     contraction, so no data is permuted anywhere.
 //   * O accumulates per lane for one query, so the rescale by exp2(m_old - m_new)
 //     is a per-lane scalar multiply.  exp2 with log2(e) folded into the scale.
 //   * The reference max only moves when a tile's max exceeds it by more than 8
 //     (log2 units); O / l is unchanged by the choice of reference and P stays
 //     below 2^8 ("FlashAttention 1–4 ...", section "FlashAttention-4",
 //     conditional rescaling).  Most tiles skip the O rescale entirely.
-//   * K/V tiles are double-buffered in LDS: the next tile's global loads are in
-//     flight in registers while the current tile is computed, one barrier per tile.
+//   * K/V tiles go from global memory straight into LDS (buffer loads with the
+//     LDS bit, 16 bytes per lane, no register staging), double-buffered: the next
+//     tile is in flight while the current one is computed, one barrier per tile.
+//     The 16-byte chunks of each key row are XOR-swizzled by key so that both the
+//     K operand reads (16 keys, one chunk) and the transposing V reads (4 keys, 4
+//     chunks) hit distinct LDS banks.
 //   * Causal: tiles past a block's last row are never loaded or computed; a wave
 //     whose rows cannot see any key of a tile skips it; element masks are applied
 //     only on tiles that cross a wave's smallest key limit (the diagonal, the
@@ -42,6 +47,8 @@
 //     time-first, "FlashAttention 1–4 ...", section "FlashAttention-4").  With
 //     round-robin dispatch over the 8 XCDs, each XCD then sees a fixed subset
 //     of heads, and concurrently running workgroups read different heads.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -53,85 +60,34 @@ constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = 32;                  // query rows per wave
 constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
 constexpr int kBK = 64;                   // keys per K/V tile
-constexpr int kPad = 8;                   // bf16 padding per LDS row (bank spread)
 constexpr float kStaleMax = 8.0f;         // log2 units
+constexpr int kDmaBytes = kWave * 16;     // one wave-wide 16-byte-per-lane LDS load
 
 template <int D>
 struct Tile {
-    static constexpr int kStride = D + kPad;   // K: [key][dim] rows
-    static constexpr int vStride = kBK + kPad; // V^T: [dim][key position] rows
-    static constexpr int kElems = kBK * kStride;
-    static constexpr int vElems = D * vStride;
-    static constexpr int stageElems = kElems + vElems;
-    static constexpr int kChunks = kBK * D / 8;      // 16-byte chunks of a K tile
-    static constexpr int kLoads = kChunks / kThreads;
-    static constexpr int vUnits = (kBK / 8) * (D / 4); // (key group of 8, 4-dim chunk)
-    static_assert(kChunks % kThreads == 0, "K tile must split evenly over the workgroup");
-    static_assert(vUnits <= kThreads, "one V unit per thread at most");
+    static constexpr int kRow = D * 2;              // bytes per key row
+    static constexpr int kBytes = kBK * kRow;       // one K or V tile
+    static constexpr int kStage = 2 * kBytes;       // K tile then V tile
+    static constexpr int kBlocks = kBytes / kDmaBytes;
+    static constexpr int kPerWave = kBlocks / kWaves;
+    static_assert(kBlocks % kWaves == 0, "tile must split evenly over the waves");
 };
 
-// Key held at V^T position p: positions 16*ks + 8*g + s (k-step ks, lane half g,
-// slot s) carry key 16*ks + 8*(s/4) + 4*g + (s%4), the row order in which the
-// 32x32 accumulator of S^T = K Q^T hands keys to lane half g.
-__device__ __forceinline__ int group_key(int j, int s) {
-    return 16 * (j >> 1) + 4 * (j & 1) + (s < 4 ? s : s + 4);
-}
-
+// 16-byte chunk c of key row `key` sits in slot c ^ swz(key) of that row.
 template <int D>
-struct Prefetch {
-    u32x4 k[Tile<D>::kLoads];
-    u32x2 v[8];
-};
-
-// Global -> registers for K/V tile starting at key kv0.  Rows past N read as
-// zeros through the buffer range check, so no load is predicated.
-template <int D>
-__device__ __forceinline__ void load_tile(Prefetch<D>& pf, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                          int kv0, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-        const int ci = tid + i * kThreads;
-        const int row = ci / (D / 8), col8 = ci % (D / 8);
-        const uint32_t off = ((uint32_t)(kv0 + row) * D + col8 * 8) * 2u;
-        pf.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-    }
-    if (tid < T::vUnits) {
-        const int j = tid % (kBK / 8), c = tid / (kBK / 8);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t off = ((uint32_t)(kv0 + group_key(j, s)) * D + 4 * c) * 2u;
-            pf.v[s] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0));
-        }
+__device__ __forceinline__ int swz(int key) {
+    if constexpr (D == 128) {
+        return ((key & 3) << 2) | ((key >> 2) & 3);
+    } else {
+        const int h = (key >> 1) & 7;
+        return ((h & 1) << 2) | (h >> 1);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const Prefetch<D>& pf, bf16* __restrict__ stage, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-        const int ci = tid + i * kThreads;
-        const int row = ci / (D / 8), col8 = ci % (D / 8);
-        *reinterpret_cast<u32x4*>(stage + row * T::kStride + col8 * 8) = pf.k[i];
-    }
-    if (tid < T::vUnits) {
-        const int j = tid % (kBK / 8), c = tid / (kBK / 8);
-        bf16* vt = stage + T::kElems + (4 * c) * T::vStride + 8 * j;
-        // 8 keys x 4 dims in registers -> 4 dims x 8 keys in LDS
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            u32x4 out;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t a = (e < 2) ? pf.v[2 * p].x : pf.v[2 * p].y;
-                const uint32_t b = (e < 2) ? pf.v[2 * p + 1].x : pf.v[2 * p + 1].y;
-                out[p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-            }
-            *reinterpret_cast<u32x4*>(vt + e * T::vStride) = out;
-        }
-    }
-}
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
@@ -139,10 +95,11 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                 bf16* __restrict__ O, float* __restrict__ LSE,
                 int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * T::stageElems];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[kWaves];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
 
     const int G = gridDim.x, bid = blockIdx.x;
@@ -153,8 +110,38 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     const int b = bh / H;
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * D * 2u;
-    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V + head, head_bytes);
+
+    // Global offset (relative to the tile's first key) each lane fetches for its DMA blocks.
+    uint32_t dma_off[T::kPerWave];
+#pragma unroll
+    for (int i = 0; i < T::kPerWave; ++i) {
+        const int p = (i * kWaves + w) * kDmaBytes + 16 * lane;
+        const int row = p / T::kRow, slot = (p % T::kRow) / 16;
+        dma_off[i] = (uint32_t)(row * T::kRow + 16 * (slot ^ swz<D>(row)));
+    }
+    // Buffer descriptors over this head's K and V rows (reads past N return zeros).
+    // The LDS loads are issued from inline assembly so that the compiler, which
+    // cannot tell the next stage from the current one, does not wait for them before
+    // every LDS read of the current tile; completion is awaited explicitly before
+    // the barrier that publishes the stage.  M0 carries the LDS destination.
+    auto desc = [&](const bf16* p) {
+        const uint64_t a = (uint64_t)(uintptr_t)p;
+        return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)head_bytes, 0x00020000};
+    };
+    const i32x4 kdesc = desc(K + head), vdesc = desc(V + head);
+    auto dma_tile = [&](int stage, int kv0) {
+        const uint32_t base = (uint32_t)kv0 * T::kRow;
+#pragma unroll
+        for (int i = 0; i < T::kPerWave; ++i) {
+            const uint32_t kd = (uint32_t)(uintptr_t)(lds_ptr)(smem + stage * T::kStage + (i * kWaves + w) * kDmaBytes);
+            const uint32_t voff = base + dma_off[i];
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(__builtin_amdgcn_readfirstlane(kd)), "v"(voff), "s"(kdesc) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(__builtin_amdgcn_readfirstlane(kd + T::kBytes)), "v"(voff), "s"(vdesc)
+                         : "memory", "m0");
+        }
+    };
 
     const int q0 = qb * kBQ;
     const int qrow = q0 + w * kQPW + col;
@@ -178,23 +165,41 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
     const int ntiles = (kv_end + kBK - 1) / kBK;
 
+    // LDS byte offsets of this lane's MFMA operands inside a stage.
+    // K (A of S^T = K Q^T): key col (+32 per slab), chunk 2 kk + half.
+    int koff[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * T::kRow + 16 * ((2 * kk + half) ^ swz<D>(col));
+    // V (A of O^T += V^T P^T) through ds_read_b64_tr_b16: lane 16 G + j addresses key
+    // 16 ks + 8 hs + 4 (G / 2) + j / 4 at dims 32 d32 + 16 (G % 2) + 4 (j % 4) .. +3; the
+    // transposing read hands lane 16 G + i the dim 32 d32 + 16 (G % 2) + i of those 4 keys.
+    int voff[D / 32][2];
+    {
+        const int G4 = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int key = 8 * hs + 4 * (G4 >> 1) + (j >> 2);
+#pragma unroll
+            for (int d32 = 0; d32 < D / 32; ++d32) {
+                const int dim = 32 * d32 + 16 * (G4 & 1) + 4 * (j & 3);
+                voff[d32][hs] = T::kBytes + key * T::kRow + 16 * ((dim >> 3) ^ swz<D>(key)) + 2 * (dim & 7);
+            }
+        }
+    }
+
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
     float m_ref = -INFINITY, l_sum = 0.f;
 
-    Prefetch<D> pf;
-    if (ntiles > 0) {
-        load_tile<D>(pf, krs, vrs, 0, tid);
-        store_tile<D>(pf, smem, tid);
-    }
+    if (ntiles > 0) dma_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        if (more) load_tile<D>(pf, krs, vrs, (t + 1) * kBK, tid);
-        const bf16* Ks = smem + (t & 1) * T::stageElems;
-        const bf16* Vts = Ks + T::kElems;
+    auto step = [&](auto stage_c, int t) {
+        constexpr int st = decltype(stage_c)::value;
+        if (t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
+        const char* Sb = smem + st * T::kStage;
         const int kv0 = t * kBK;
 
         if (kv0 < wmax) {
@@ -205,11 +210,10 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    const bf16* kp = Ks + (sub * 32 + col) * T::kStride + 8 * half;
+                for (int sub = 0; sub < 2; ++sub)
                     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8*>(kp + 16 * kk), qf[kk], s[sub], 0, 0, 0);
-                }
+                        *reinterpret_cast<const bf16x8*>(Sb + sub * 32 * T::kRow + koff[kk]), qf[kk], s[sub], 0, 0,
+                        0);
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
@@ -258,14 +262,22 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
-                    const bf16* vp = Vts + (32 * d32 + col) * T::vStride + 8 * half;
-                    oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8*>(vp + 16 * ks), __builtin_bit_cast(bf16x8, pk[ks]),
-                        oacc[d32], 0, 0, 0);
+                    const char* vb = Sb + 16 * ks * T::kRow;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + voff[d32][0]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + voff[d32][1]));
+                    const u32x4 a = {__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                     __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+                    oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                        __builtin_bit_cast(bf16x8, pk[ks]),
+                                                                        oacc[d32], 0, 0, 0);
                 }
         }
-        if (more) store_tile<D>(pf, smem + ((t + 1) & 1) * T::stageElems, tid);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
     }
 
     // Epilogue: one division per row; each lane half summed its own keys.
