@@ -10,11 +10,14 @@ module compiles it with gcc and calls it through ctypes.  What it computes and
 which passages it follows are stated in the header of ``fa_oracle.c``:
 O = softmax(scale * Q K^T + M) V and LSE = log sum exp(scale * Q K^T + M) per
 row, M being 0 on valid keys and -inf elsewhere, a row with no valid key giving
-O = 0 and LSE = -inf.
+O = 0 and LSE = -inf; and the backward pass, the gradients dQ, dK, dV of
+sum(dO * O) for a given dO, by the chain rule through the row softmax
+(optionally with the row term D_i = <dO_i, O_i> taken from a caller's stored O).
 
-Parity: every function here is pinned by ``tests/test_oracle.py`` against the
-pages' worked examples, closed forms, invariants and brute force; none is
-"parity unpinned".
+Parity: every function here is pinned, by ``tests/test_oracle.py`` (forward)
+and ``tests/test_oracle_bwd.py`` (backward), against the pages' worked
+examples, closed forms, invariants, finite differences and brute force; none
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -55,6 +58,13 @@ def load(path: str = LIBRARY):
     lib.fa_oracle_rows.restype = ctypes.c_int
     lib.fa_oracle_max_threads.argtypes = []
     lib.fa_oracle_max_threads.restype = ctypes.c_int
+    lib.fa_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                  ctypes.c_int, ctypes.c_double, ip, ctypes.c_int]
+    lib.fa_oracle_bwd.restype = ctypes.c_int
+    lib.fa_oracle_bwd_sample.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_double, ip, i64, i64,
+                                         i64, lp, i64, lp, dp, dp, dp, ctypes.c_int]
+    lib.fa_oracle_bwd_sample.restype = ctypes.c_int
     return lib
 
 
@@ -135,3 +145,72 @@ def attention_rows(q, k, v, row_ids, causal: bool = False, scale: Optional[float
 
 def max_threads() -> int:
     return int(_library().fa_oracle_max_threads())
+
+
+def attention_bwd(q, k, v, dout, causal: bool = False, scale: Optional[float] = None,
+                  kv_limit=None, nthreads: int = 0, lib=None, o=None):
+    """Gradients of sum(dout * O) with respect to q, k, v, all of shape (B, H, N, d).
+
+    With o (B, H, N, d) given, the row term D_i is <dout_i, o_i> from that
+    output instead of the exact one.  Returns (dq, dk, dv) as float64 arrays of
+    the same shape.
+    """
+    lib = lib or _library()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if q.ndim != 4 or any(a.shape != q.shape for a in (k, v, dout)):
+        raise ValueError("q, k, v, dout must share one (B, H, N, d) shape")
+    o_p = None
+    if o is not None:
+        o = _f64(o)
+        if o.shape != q.shape:
+            raise ValueError("o must have the shape of q")
+        o_p = _ptr(o, ctypes.c_double)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lim, lim_p = _limits(kv_limit, B, N)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    rc = lib.fa_oracle_bwd(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                           _ptr(dout, ctypes.c_double), o_p, _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                           _ptr(dv, ctypes.c_double), B, H, N, d, int(bool(causal)), float(scale), lim_p,
+                           int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_bwd failed ({rc})")
+    return dq, dk, dv
+
+
+def attention_bwd_sample(q, k, v, dout, b: int, h: int, q_rows, k_rows, causal: bool = False,
+                         scale: Optional[float] = None, kv_limit=None, nthreads: int = 0, lib=None,
+                         o_head=None):
+    """Sampled gradients of one head (b, h): dq at query rows q_rows, dk and dv at key rows k_rows.
+
+    Rows are indices within the head.  With o_head (N, d) given, D_i is
+    <dout_i, o_head_i>.  Returns (dq, dk, dv) of shapes (len(q_rows), d),
+    (len(k_rows), d), (len(k_rows), d).
+    """
+    lib = lib or _library()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    o_p = None
+    if o_head is not None:
+        o_head = _f64(o_head)
+        if o_head.shape != (N, d):
+            raise ValueError("o_head must have shape (N, d)")
+        o_p = _ptr(o_head, ctypes.c_double)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lim, lim_p = _limits(kv_limit, B, N)
+    qr = np.ascontiguousarray(q_rows, dtype=np.int64)
+    kr = np.ascontiguousarray(k_rows, dtype=np.int64)
+    dq = np.empty((qr.size, d), np.float64)
+    dk = np.empty((kr.size, d), np.float64)
+    dv = np.empty((kr.size, d), np.float64)
+    rc = lib.fa_oracle_bwd_sample(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                                  _ptr(dout, ctypes.c_double), o_p, B, H, N, d, int(bool(causal)), float(scale),
+                                  lim_p,
+                                  int(b), int(h), qr.size, _ptr(qr, ctypes.c_int64), kr.size,
+                                  _ptr(kr, ctypes.c_int64), _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                                  _ptr(dv, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_bwd_sample failed ({rc})")
+    return dq, dk, dv

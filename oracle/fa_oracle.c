@@ -185,3 +185,228 @@ int fa_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass (gradients of the forward above).
+ *
+ * Given the upstream gradient dO (same shape as O), the gradients of the
+ * scalar sum_i <dO_i, O_i> with respect to Q, K and V.  Written out with the
+ * chain rule through the row softmax, all in fp64 from the exact inputs:
+ *   P_ij  = exp(s_ij - lse_i) on valid keys, 0 elsewhere (0 for a row with no
+ *           valid key);
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = <dO_i, V_j>
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij K_j
+ *   dK_j  = scale * sum_i dS_ij Q_i
+ * Sources on the pages: the backward pass recomputes S and P = exp(S - L)
+ * block by block from the saved Q, K, V, O and L, without an online softmax
+ * ("GPU 与 TPU：让硬件不再是黑魔法" §11.5, part 3); the saved statistic is
+ * L = m + log(l) ("FlashAttention 1–4 ...", section "FlashAttention-2").  The
+ * pages do not print the gradient formulas; the lines above are the chain
+ * rule, pinned in the tests against central finite differences of
+ * fa_oracle_fwd.  Here D_i is formed from P and dP, the definition.  Since
+ * O_i = sum_j P_ij V_j, D_i also equals <dO_i, O_i>; a backward pass that is
+ * handed a stored O (rounded to the storage type) forms D_i from it.  When the
+ * caller passes such an O (o_given, non-null), D_i = <dO_i, o_given_i> instead,
+ * so that the result is exactly the gradient that a pass consuming that O
+ * computes.
+ * ------------------------------------------------------------------------ */
+
+/* lse and D of every row of one head: lse_h[N], dd_h[N]. s scratch of N. */
+static void head_row_stats(const double *q, const double *k, const double *v, const double *dout,
+                           const double *o_given, int64_t H, int64_t N, int64_t d, int causal, double scale,
+                           const int32_t *kv_limit, int64_t b, int64_t h,
+                           double *lse_h, double *dd_h, double *s, double *orow)
+{
+    const double *vh = v + (b * H + h) * N * d;
+    const double *dh = dout + (b * H + h) * N * d;
+    for (int64_t i = 0; i < N; ++i) {
+        one_row(q, k, v, orow, &lse_h[i], H, N, d, causal, scale, kv_limit, b, h, i, s);
+        int64_t limit = kv_limit ? (int64_t)kv_limit[b * N + i] : N;
+        if (limit > N) limit = N;
+        double acc = 0.0;
+        if (lse_h[i] != -INFINITY && !o_given) {
+            /* one_row left the scores in s */
+            for (int64_t j = 0; j < N; ++j) {
+                if (!key_is_valid(j, i, causal, limit)) continue;
+                double p = exp(s[j] - lse_h[i]);
+                double dp = 0.0;
+                for (int64_t c = 0; c < d; ++c) dp += dh[i * d + c] * vh[j * d + c];
+                acc += p * dp;
+            }
+        } else if (lse_h[i] != -INFINITY) {
+            const double *oh = o_given + (b * H + h) * N * d;
+            for (int64_t c = 0; c < d; ++c) acc += dh[i * d + c] * oh[i * d + c];
+        }
+        dd_h[i] = acc;
+    }
+}
+
+/* Full gradients.  dq, dk, dv are [B, H, N, d]; o_given is null or a
+ * [B, H, N, d] output to form D from.  Heads run in parallel, rows of a head in
+ * order (dK and dV accumulate over rows).  Returns 0 or -1. */
+int fa_oracle_bwd(const double *q, const double *k, const double *v, const double *dout,
+                  const double *o_given, double *dq, double *dk, double *dv,
+                  int64_t B, int64_t H, int64_t N, int64_t d,
+                  int causal, double scale, const int32_t *kv_limit, int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 0 || H < 0 || N < 0 || d <= 0) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel num_threads(nt)
+    {
+        const size_t n1 = (size_t)(N > 0 ? N : 1);
+        double *s = (double *)malloc(n1 * sizeof(double));
+        double *lse_h = (double *)malloc(n1 * sizeof(double));
+        double *dd_h = (double *)malloc(n1 * sizeof(double));
+        double *orow = (double *)malloc((size_t)d * sizeof(double));
+        if (!s || !lse_h || !dd_h || !orow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                const int64_t b = bh / H, h = bh % H;
+                const double *qh = q + bh * N * d, *kh = k + bh * N * d, *vh = v + bh * N * d;
+                const double *dh = dout + bh * N * d;
+                double *dqh = dq + bh * N * d, *dkh = dk + bh * N * d, *dvh = dv + bh * N * d;
+                head_row_stats(q, k, v, dout, o_given, H, N, d, causal, scale, kv_limit, b, h, lse_h, dd_h, s,
+                               orow);
+                for (int64_t e = 0; e < N * d; ++e) { dqh[e] = 0.0; dkh[e] = 0.0; dvh[e] = 0.0; }
+                for (int64_t i = 0; i < N; ++i) {
+                    if (lse_h[i] == -INFINITY) continue;
+                    int64_t limit = kv_limit ? (int64_t)kv_limit[b * N + i] : N;
+                    if (limit > N) limit = N;
+                    for (int64_t j = 0; j < N; ++j) {
+                        if (!key_is_valid(j, i, causal, limit)) continue;
+                        double sij = 0.0, dp = 0.0;
+                        for (int64_t c = 0; c < d; ++c) {
+                            sij += qh[i * d + c] * kh[j * d + c];
+                            dp += dh[i * d + c] * vh[j * d + c];
+                        }
+                        const double p = exp(scale * sij - lse_h[i]);
+                        const double ds = p * (dp - dd_h[i]);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dvh[j * d + c] += p * dh[i * d + c];
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qh[i * d + c];
+                        }
+                    }
+                }
+            }
+        }
+        free(s); free(lse_h); free(dd_h); free(orow);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Sampled gradients of one head (b, h): dq for nq query rows, dk and dv for nk
+ * key rows.  Rows are head-local indices.  dq_out [nq, d], dk_out and dv_out
+ * [nk, d]; o_head is null or the head's [N, d] output to form D from.  Cost: the
+ * head's row statistics (two passes over all rows) plus the sampled sums.
+ * Returns 0 or -1. */
+int fa_oracle_bwd_sample(const double *q, const double *k, const double *v, const double *dout,
+                         const double *o_head, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int causal, double scale, const int32_t *kv_limit,
+                         int64_t b, int64_t h, int64_t nq, const int64_t *q_rows,
+                         int64_t nk, const int64_t *k_rows,
+                         double *dq_out, double *dk_out, double *dv_out, int nthreads)
+{
+    if (!q || !k || !v || !dout || b < 0 || b >= B || h < 0 || h >= H || N <= 0 || d <= 0) return -1;
+    for (int64_t t = 0; t < nq; ++t) if (q_rows[t] < 0 || q_rows[t] >= N) return -1;
+    for (int64_t t = 0; t < nk; ++t) if (k_rows[t] < 0 || k_rows[t] >= N) return -1;
+    const int64_t bh = b * H + h;
+    const double *qh = q + bh * N * d, *kh = k + bh * N * d, *vh = v + bh * N * d, *dh = dout + bh * N * d;
+    double *lse_h = (double *)malloc((size_t)N * sizeof(double));
+    double *dd_h = (double *)malloc((size_t)N * sizeof(double));
+    if (!lse_h || !dd_h) { free(lse_h); free(dd_h); return -1; }
+    int failed = 0;
+#ifdef _OPENMP
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+    /* row statistics, rows in parallel */
+#pragma omp parallel num_threads(nt)
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        double *orow = (double *)malloc((size_t)d * sizeof(double));
+        if (!s || !orow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t i = 0; i < N; ++i) {
+                one_row(q, k, v, orow, &lse_h[i], H, N, d, causal, scale, kv_limit, b, h, i, s);
+                int64_t limit = kv_limit ? (int64_t)kv_limit[b * N + i] : N;
+                if (limit > N) limit = N;
+                double acc = 0.0;
+                if (lse_h[i] != -INFINITY && !o_head) {
+                    for (int64_t j = 0; j < N; ++j) {
+                        if (!key_is_valid(j, i, causal, limit)) continue;
+                        double dp = 0.0;
+                        for (int64_t c = 0; c < d; ++c) dp += dh[i * d + c] * vh[j * d + c];
+                        acc += exp(s[j] - lse_h[i]) * dp;
+                    }
+                } else if (lse_h[i] != -INFINITY) {
+                    for (int64_t c = 0; c < d; ++c) acc += dh[i * d + c] * o_head[i * d + c];
+                }
+                dd_h[i] = acc;
+            }
+        }
+        free(s); free(orow);
+    }
+    if (failed) { free(lse_h); free(dd_h); return -1; }
+    /* dq rows: sum over keys */
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t t = 0; t < nq; ++t) {
+        const int64_t i = q_rows[t];
+        double *out = dq_out + t * d;
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        if (lse_h[i] == -INFINITY) continue;
+        int64_t limit = kv_limit ? (int64_t)kv_limit[b * N + i] : N;
+        if (limit > N) limit = N;
+        for (int64_t j = 0; j < N; ++j) {
+            if (!key_is_valid(j, i, causal, limit)) continue;
+            double sij = 0.0, dp = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                sij += qh[i * d + c] * kh[j * d + c];
+                dp += dh[i * d + c] * vh[j * d + c];
+            }
+            const double ds = exp(scale * sij - lse_h[i]) * (dp - dd_h[i]);
+            for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * kh[j * d + c];
+        }
+    }
+    /* dk, dv rows: sums over queries */
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t t = 0; t < nk; ++t) {
+        const int64_t j = k_rows[t];
+        double *ok = dk_out + t * d, *ov = dv_out + t * d;
+        for (int64_t c = 0; c < d; ++c) { ok[c] = 0.0; ov[c] = 0.0; }
+        for (int64_t i = 0; i < N; ++i) {
+            if (lse_h[i] == -INFINITY) continue;
+            int64_t limit = kv_limit ? (int64_t)kv_limit[b * N + i] : N;
+            if (limit > N) limit = N;
+            if (!key_is_valid(j, i, causal, limit)) continue;
+            double sij = 0.0, dp = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                sij += qh[i * d + c] * kh[j * d + c];
+                dp += dh[i * d + c] * vh[j * d + c];
+            }
+            const double p = exp(scale * sij - lse_h[i]);
+            const double ds = p * (dp - dd_h[i]);
+            for (int64_t c = 0; c < d; ++c) {
+                ov[c] += p * dh[i * d + c];
+                ok[c] += scale * ds * qh[i * d + c];
+            }
+        }
+    }
+    free(lse_h); free(dd_h);
+    return 0;
+}
