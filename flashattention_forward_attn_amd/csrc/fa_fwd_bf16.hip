@@ -47,10 +47,9 @@
 //     time-first, "FlashAttention 1–4 ...", section "FlashAttention-4").  With
 //     round-robin dispatch over the 8 XCDs, each XCD then sees a fixed subset
 //     of heads, and concurrently running workgroups read different heads.
-#include <type_traits>
-
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace fused_bf16 {
@@ -61,7 +60,6 @@ constexpr int kQPW = 32;                  // query rows per wave
 constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
 constexpr int kBK = 64;                   // keys per K/V tile
 constexpr float kStaleMax = 8.0f;         // log2 units
-constexpr int kDmaBytes = kWave * 16;     // one wave-wide 16-byte-per-lane LDS load
 
 template <int D>
 struct Tile {
@@ -73,21 +71,6 @@ struct Tile {
     static_assert(kBlocks % kWaves == 0, "tile must split evenly over the waves");
 };
 
-// 16-byte chunk c of key row `key` sits in slot c ^ swz(key) of that row.
-template <int D>
-__device__ __forceinline__ int swz(int key) {
-    if constexpr (D == 128) {
-        return ((key & 3) << 2) | ((key >> 2) & 3);
-    } else {
-        const int h = (key >> 1) & 7;
-        return ((h & 1) << 2) | (h >> 1);
-    }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
@@ -119,27 +102,15 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const int row = p / T::kRow, slot = (p % T::kRow) / 16;
         dma_off[i] = (uint32_t)(row * T::kRow + 16 * (slot ^ swz<D>(row)));
     }
-    // Buffer descriptors over this head's K and V rows (reads past N return zeros).
-    // The LDS loads are issued from inline assembly so that the compiler, which
-    // cannot tell the next stage from the current one, does not wait for them before
-    // every LDS read of the current tile; completion is awaited explicitly before
-    // the barrier that publishes the stage.  M0 carries the LDS destination.
-    auto desc = [&](const bf16* p) {
-        const uint64_t a = (uint64_t)(uintptr_t)p;
-        return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)head_bytes, 0x00020000};
-    };
-    const i32x4 kdesc = desc(K + head), vdesc = desc(V + head);
+    // K/V tiles go to LDS with direct buffer loads (reads past N return zeros).
+    const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
     auto dma_tile = [&](int stage, int kv0) {
         const uint32_t base = (uint32_t)kv0 * T::kRow;
 #pragma unroll
         for (int i = 0; i < T::kPerWave; ++i) {
-            const uint32_t kd = (uint32_t)(uintptr_t)(lds_ptr)(smem + stage * T::kStage + (i * kWaves + w) * kDmaBytes);
-            const uint32_t voff = base + dma_off[i];
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :: "s"(__builtin_amdgcn_readfirstlane(kd)), "v"(voff), "s"(kdesc) : "memory", "m0");
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :: "s"(__builtin_amdgcn_readfirstlane(kd + T::kBytes)), "v"(voff), "s"(vdesc)
-                         : "memory", "m0");
+            const uint32_t kd = lds_addr(smem + stage * T::kStage + (i * kWaves + w) * kDmaBytes);
+            dma16(kdesc, kd, base + dma_off[i]);
+            dma16(vdesc, kd + T::kBytes, base + dma_off[i]);
         }
     };
 
@@ -263,10 +234,8 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
                     const char* vb = Sb + 16 * ks * T::kRow;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + voff[d32][0]));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + voff[d32][1]));
-                    const u32x4 a = {__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
-                                     __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+                    const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
+                    const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
                     oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                                         __builtin_bit_cast(bf16x8, pk[ks]),
                                                                         oacc[d32], 0, 0, 0);

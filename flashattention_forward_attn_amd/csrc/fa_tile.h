@@ -1,0 +1,72 @@
+// fa_tile.h -- LDS tile helpers shared by the bf16 kernels (forward and backward):
+// direct global -> LDS loads, the XOR chunk swizzle of a tile row, and the
+// transposing LDS read.
+#pragma once
+
+#include <type_traits>
+
+#include "fa_common.h"
+
+namespace fa {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kDmaBytes = kWave * 16;  // one wave-wide 16-byte-per-lane LDS load
+
+// Rows of D bf16 values are stored in LDS as D/8 chunks of 16 bytes; chunk c of
+// row `row` sits in slot c ^ swz<D>(row).  With this swizzle a read of one chunk
+// from 16 consecutive rows, and a read of 4 chunks from 4 consecutive rows (the
+// transposing-read pattern), each touch 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        const int h = (row >> 1) & 7;
+        return ((h & 1) << 2) | (h >> 1);
+    }
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr)p; }
+
+// Buffer descriptor over [base, base + bytes) as four scalars: reads past the
+// end return zeros.
+__device__ __forceinline__ i32x4 dma_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Wave-wide load straight into LDS: lane l's 16 bytes at global offset voff land at
+// LDS byte address dst + 16 l (M0 holds dst).  Issued from inline assembly so that
+// the compiler does not wait for it before unrelated LDS reads; the caller waits
+// with s_waitcnt vmcnt before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(const i32x4& desc, uint32_t dst, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc) : "memory", "m0");
+}
+// The same with 4 bytes per lane (lane l's word lands at dst + 4 l).
+__device__ __forceinline__ void dma4(const i32x4& desc, uint32_t dst, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc) : "memory", "m0");
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives, in
+// slot s, element i % 4 of the 8 bytes addressed by lane 4 s + i / 4.
+__device__ __forceinline__ u32x2 tr_read(const char* p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    return __builtin_bit_cast(u32x2, r);
+}
+
+}  // namespace fa
