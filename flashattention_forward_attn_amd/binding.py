@@ -47,6 +47,10 @@ def load(path: str = LIBRARY):
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_unfused_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_unfused_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]
+    lib.fa_bwd_bf16.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -117,6 +121,37 @@ def fa_fwd_unfused_f32(q, k, v, o, lse, causal: bool, scale: float, kv_limit=Non
     _check(load().fa_fwd_unfused_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      int(bool(causal)), float(scale), _ptr(kv_limit), _ptr(workspace), nbytes,
                                      _stream(stream)))
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N))
+
+
+def fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float, kv_limit=None, workspace=None,
+                stream=None) -> None:
+    """Backward pass of fa_fwd_bf16: bf16 [B, H, N, d] tensors, lse fp32 [B, H, N]; workspace a device
+    uint8 tensor of at least fa_bwd_workspace_bytes(B, H, N) bytes."""
+    B, H, N, d = _dims(q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().fa_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit),
+                              _ptr(workspace), nbytes, _stream(stream)))
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: Optional[float] = None,
+                       kv_limit=None, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run the backward pass (bf16).
+    Returns (dq, dk, dv)."""
+    import torch
+    B, H, N, d = _dims(q)
+    if scale is None:
+        scale = d ** -0.5
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"the backward pass takes bf16 tensors, got {q.dtype}")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=q.device)
+    fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, kv_limit, ws, stream)
+    return dq, dk, dv
 
 
 def attention(q, k, v, causal: bool = False, scale: Optional[float] = None, kv_limit=None, unfused: bool = False,

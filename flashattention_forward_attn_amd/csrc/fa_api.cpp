@@ -89,6 +89,11 @@ fa_status unfused(bool bf16_path, const void* q, const void* k, const void* v, v
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t bwd_workspace_bytes(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return (size_t)(2 * fa::bwd_stats_floats(B, H, N) * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +130,39 @@ fa_status fa_fwd_unfused_f32(const float* q, const float* k, const float* v, flo
                              size_t workspace_bytes_given, void* stream) {
     return unfused(false, q, k, v, o, lse, B, H, N, d, causal, scale, kv_limit, workspace, workspace_bytes_given,
                    stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) { return bwd_workspace_bytes(B, H, N); }
+
+fa_status fa_bwd_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o, const fa_bf16* dout,
+                      const float* lse, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv, int B, int H, int N, int d, int causal,
+                      float scale, const int32_t* kv_limit, void* workspace, size_t workspace_bytes_given,
+                      void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    const int64_t elems = (int64_t)B * H * N * d;
+    if (elems > INT32_MAX) return FA_ERR_SHAPE;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o, (const void*)dout,
+                          (const void*)dq, (const void*)dk, (const void*)dv})
+        if (!aligned(p, 16)) return FA_ERR_ALIGN;
+    if (!aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4))) return FA_ERR_ALIGN;
+    const size_t need = bwd_workspace_bytes(B, H, N);
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, kWsAlign)) return FA_ERR_WORKSPACE;
+    const int64_t tbytes = elems * 2;
+    const Range ins[] = {span(q, tbytes), span(k, tbytes), span(v, tbytes), span(o, tbytes), span(dout, tbytes),
+                         span(lse, (int64_t)B * H * N * 4), span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0)};
+    const Range outs[] = {span(dq, tbytes), span(dk, tbytes), span(dv, tbytes), span(workspace, (int64_t)need)};
+    for (int i = 0; i < 4; ++i) {
+        for (Range in : ins)
+            if (overlap(outs[i], in)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+    }
+    return hip_status(fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal != 0, scale,
+                                          kv_limit, static_cast<float*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 const char* fa_status_str(fa_status s) {

@@ -25,4 +25,13 @@ hipError_t launch_unfused(bool bf16_path, const void* q, const void* k, const vo
                           int B, int H, int N, int d, bool causal, float scale, const int32_t* kv_limit,
                           float* S, void* P, hipStream_t stream);
 
+// Backward pass: floats per statistic in the workspace (D and the base-2 LSE,
+// each B*H*N, the count rounded up to 64 so the second starts 256-byte aligned).
+inline int64_t bwd_stats_floats(int B, int H, int N) { return ((int64_t)B * H * N + 63) / 64 * 64; }
+
+// Three launches: row statistics, dK/dV, dQ.  workspace holds 2 * bwd_stats_floats.
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, bool causal,
+                           float scale, const int32_t* kv_limit, float* workspace, hipStream_t stream);
+
 }  // namespace fa

@@ -12,6 +12,11 @@ Draw order for every workload: Q, K, V (each a float64 standard normal of
 shape (B, H, N, d), cast to float32), then, for the key-padding workload, the
 per-batch valid lengths, the batch item that gets a fully masked query block,
 and that block's start.  All draws come from ``numpy.random.default_rng(seed)``.
+
+For the backward pass, the upstream gradient dO (same shape as O, standard
+normal, float64 cast to float32, then rounded like the other inputs) comes from
+its own stream, ``numpy.random.default_rng([seed, 1])``, so the forward inputs
+are unchanged by it.
 """
 from __future__ import annotations
 
@@ -68,6 +73,12 @@ class Workload:
     def flops(self) -> float:
         """Nominal forward FLOPs: two N x N x d contractions per head, halved when causal."""
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """Nominal backward FLOPs: five N x N x d contractions per head (the
+        recomputed scores, dV, dP, dQ and dK), halved when causal."""
+        f = 10.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
     def describe(self) -> dict:
@@ -165,3 +176,24 @@ def random_kv_limit(B: int, N: int, seed: int, kind: str) -> np.ndarray:
     elif kind != "random":
         raise ValueError(kind)
     return lim
+
+
+@dataclasses.dataclass
+class GradOutput:
+    dout: np.ndarray                       # float32 values (exactly bf16 values for bf16 workloads)
+    dout_bits: Optional[np.ndarray] = None  # uint16 bf16 bits (bf16 workloads)
+
+    def digest(self) -> str:
+        return hashlib.sha256(np.ascontiguousarray(self.dout).tobytes()).hexdigest()
+
+
+def grad_output(w: Workload, seed: Optional[int] = None) -> GradOutput:
+    """The upstream gradient dO for the backward pass (its own random stream)."""
+    rng = np.random.default_rng([w.seed if seed is None else seed, 1])
+    g = rng.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
+    if w.dtype == "bf16":
+        bits = bf16_bits(g)
+        return GradOutput(bf16_to_f32(bits), bits)
+    if w.dtype == "f32":
+        return GradOutput(g, None)
+    raise ValueError(f"unknown dtype {w.dtype!r}")

@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library (libfa.so).
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so): the
+ * forward pass (fused and unfused) and the backward pass of the fused forward.
  *
  * The operation.  For every batch item b, head h and query row i:
  *
@@ -64,7 +65,7 @@ typedef enum {
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                      */
     FA_ERR_SCALE = 4,     /* scale is NaN, infinite, zero or negative                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
-    FA_ERR_WORKSPACE = 6, /* unfused path: workspace NULL, too small or misaligned   */
+    FA_ERR_WORKSPACE = 6, /* unfused or backward path: workspace NULL, too small or misaligned */
     FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch                */
     FA_ERR_ALIAS = 8      /* an output overlaps an input, the other output or the workspace */
 } fa_status;
@@ -127,6 +128,44 @@ fa_status fa_fwd_unfused_f32(const float *q, const float *k, const float *v,
                              int B, int H, int N, int d, int causal, float scale,
                              const int32_t *kv_limit,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace the backward pass needs: two fp32 statistics per row
+ * (D_i = <dO_i, O_i> and the log-sum-exp in base 2), each B*H*N values rounded up
+ * to a multiple of 64.  Returns 0 if an argument is out of range.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * Backward pass of fa_fwd_bf16: given q, k, v, the forward's o and lse, and the
+ * gradient dout of a loss with respect to o, writes the gradients dq, dk, dv of
+ * that loss (bf16, same layout as q).  Mathematically, with P the attention
+ * probabilities of the forward (0 on masked keys and for rows with no valid key):
+ *
+ *   dv_j = sum_i P_ij dout_i,   dP_ij = <dout_i, v_j>,   D_i = <dout_i, o_i>,
+ *   dS_ij = P_ij (dP_ij - D_i),  dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
+ *
+ * P is recomputed tile by tile as exp(S - lse) from the saved statistic, with no
+ * online softmax ("GPU 与 TPU：让硬件不再是黑魔法" §11.5, part 3; "FlashAttention
+ * 1–4 ...", section "FlashAttention-2": one column block of K/V per thread block,
+ * dK and dV accumulated locally).  dq has a pass of its own instead of atomic
+ * adds, so results are deterministic.  P and dS are rounded to bf16 (nearest-even)
+ * before their contractions; accumulation is fp32.
+ *
+ * Arguments as for fa_fwd_bf16 (same causal, scale and kv_limit as the forward
+ * call that produced o and lse), plus: dout [B, H, N, d] bf16; dq, dk, dv
+ * [B, H, N, d] bf16 outputs, 16-byte aligned, overlapping no input, no other
+ * output and not the workspace; workspace at least fa_bwd_workspace_bytes(B, H, N)
+ * bytes of device memory owned by the caller, 256-byte aligned, overwritten.
+ * Errors as for the forward; FA_ERR_WORKSPACE for a missing, small or misaligned
+ * workspace.
+ */
+fa_status fa_bwd_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
+                      const fa_bf16 *o, const fa_bf16 *dout, const float *lse,
+                      fa_bf16 *dq, fa_bf16 *dk, fa_bf16 *dv,
+                      int B, int H, int N, int d, int causal, float scale,
+                      const int32_t *kv_limit,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status s);

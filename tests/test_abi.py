@@ -104,3 +104,43 @@ def test_workspace_bytes(lib):
     assert f(2, 32, 4096, 4) == 2 * 32 * 4096 * 4096 * 8
     assert f(1, 1, 3, 2) == 768 + 512  # S: 3*64*4 = 768; P: 3*64*2 = 384, rounded up to 512
     assert f(0, 1, 1, 2) == 0 and f(1, 1, 1, 3) == 0
+
+
+# backward: fake addresses for o, dout, dq, dk, dv beyond the forward's
+DO, DQ, DK, DV = (0x10000000 * (i + 8) for i in range(4))
+
+
+def bwd(lib, q=Q, k=K, v=V, o=O, g=DO, l=L, dq=DQ, dk=DK, dv=DV, ws=W, ws_bytes=None, B=2, H=3, N=100, d=128,
+        causal=0, scale=0.125, m=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N)
+    return lib.fa_bwd_bf16(q, k, v, o, g, l, dq, dk, dv, B, H, N, d, causal, scale, m, ws, ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, g=None) == 1
+    assert bwd(lib, dq=None) == 1
+    assert bwd(lib, l=None) == 1
+    assert bwd(lib, N=0) == 2
+    assert bwd(lib, B=1 << 12, H=1 << 12, N=1 << 8, d=64) == 2
+    assert bwd(lib, d=32) == 3
+    assert bwd(lib, scale=float("nan")) == 4
+    assert bwd(lib, dk=DK + 8) == 5
+    assert bwd(lib, g=DO + 4) == 5
+    assert bwd(lib, l=L + 1) == 5
+    assert bwd(lib, ws=None) == 6
+    assert bwd(lib, ws_bytes=16) == 6
+    assert bwd(lib, ws=W + 64) == 6
+    assert bwd(lib, dq=Q) == 8                 # gradient over an input
+    assert bwd(lib, dv=DK + 256) == 8          # two gradients overlap
+    assert bwd(lib, ws=DQ) == 8                # workspace over a gradient
+    assert bwd(lib, dk=L + 1024) == 8          # gradient over lse
+
+
+def test_backward_workspace_bytes(lib):
+    f = lib.fa_bwd_workspace_bytes
+    # two fp32 statistics per row, each count rounded up to 64
+    assert f(1, 1, 64) == 2 * 64 * 4
+    assert f(1, 1, 65) == 2 * 128 * 4
+    assert f(2, 32, 4096) == 2 * 2 * 32 * 4096 * 4
+    assert f(0, 1, 1) == 0 and f(1, 1, 0) == 0
