@@ -16,7 +16,14 @@ Besides the headline number the line carries:
                   scaled to TFLOP/s with the same FLOP convention;
   unfused      -- the three-kernel baseline (S and P through device memory)
                   timed the same way;
-  workloads    -- the other bf16 workloads, fused, timed the same way.
+  workloads    -- the other bf16 workloads, fused, timed the same way;
+  backward     -- the backward pass (fa_bwd_bf16: three launches) on the same
+                  workload with a seeded dO, timed the same way, with its own
+                  roofline (nominal backward FLOPs 10*B*H*N^2*d, halved for
+                  causal, per call / mean call time) and its own oracle
+                  baseline (the full fp64 backward of a few heads).
+
+--path backward makes the backward pass the timed step instead.
 """
 from __future__ import annotations
 
@@ -31,6 +38,15 @@ import numpy as np
 HEADLINE = "bf16_causal_b2h32n4096d128"
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
+BWD_METRIC = "attention bwd TFLOP/s (bf16, nominal 10*N^2*d per head) and % of MI355X MFMA peak"
+
+# Sources each timed path is built from: a traffic figure measured on other
+# sources is stale and is not reported.
+KERNEL_SOURCES = {
+    "fused": ["fa_fwd_bf16.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
+    "unfused": ["fa_unfused.hip", "fa_common.h", "fa_launch.h"],
+    "backward": ["fa_bwd_bf16.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
+}
 
 
 def host_threads() -> int:
@@ -100,6 +116,24 @@ def measure_unfused(torch, binding, x, steps, warmup):
     return ms
 
 
+def measure_backward(torch, binding, x, g, steps, warmup):
+    """Mean ms per fa_bwd_bf16 call (three launches) on O and LSE from one forward."""
+    w = x.workload
+    q, k, v, lim = device_inputs(torch, x)
+    o, lse = binding.attention(q, k, v, causal=w.causal, scale=w.scale, kv_limit=lim)
+    dout = torch.from_numpy(g.dout_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(binding.fa_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        binding.fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, w.causal, w.scale, lim, ws, stream)
+
+    ms = time_launches(torch, launch, steps, warmup)
+    del q, k, v, o, lse, lim, dout, dq, dk, dv, ws
+    return ms
+
+
 def effective_flops(x) -> float:
     """FLOPs of the valid (query, key) pairs only: 4 d per pair."""
     w = x.workload
@@ -140,6 +174,42 @@ def cpu_baseline(x, target_seconds: float):
     }
 
 
+def cpu_baseline_backward(x, g):
+    """The oracle's full fp64 backward over the first heads of batch item 0, one
+    head per host thread (the oracle runs heads in parallel)."""
+    import oracle
+    w = x.workload
+    threads = host_threads()
+    nh = min(w.H, threads)
+    sl = lambda a: np.ascontiguousarray(a[:1, :nh], dtype=np.float64)
+    q, k, v, dout = sl(x.q), sl(x.k), sl(x.v), sl(g.dout)
+    lim = None if x.kv_limit is None else np.ascontiguousarray(x.kv_limit[:1])
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q, k, v, dout, w.causal, w.scale, lim, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = w.bwd_flops() / (w.B * w.H) * nh
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nh,
+        "kind": "oracle",
+        "sample": f"full backward of heads 0..{nh - 1} of batch item 0 of {w.name}, fp64, {dt:.1f} s; "
+                  f"nominal backward FLOPs of those heads",
+        "seconds": round(dt, 3),
+    }
+
+
+def load_traffic(path_file: str, path: str, workload: str):
+    """Measured HBM bytes per launch for (path, workload), or None if absent or stale."""
+    if not os.path.exists(path_file):
+        return None
+    with open(path_file) as f:
+        t = json.load(f).get(path, {}).get(workload)
+    if t and t.get("kernel_source_sha256") == _kernel_digest(path):
+        return t.get("bytes_per_launch")
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,8 +222,9 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
-    ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
-                    help="time the fused kernel (default) or the unfused three-kernel baseline as the step")
+    ap.add_argument("--path", choices=("fused", "unfused", "backward"), default="fused",
+                    help="time the fused kernel (default), the unfused three-kernel baseline or the "
+                         "backward pass as the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
                          "its FETCH_SIZE/WRITE_SIZE calibrate the traffic counters")
@@ -183,20 +254,22 @@ def main() -> int:
     binding.load()
 
     w = inputs.WORKLOADS[args.workload]
+    if w.dtype != "bf16" and args.path == "backward":
+        print("the backward pass is bf16 only", file=sys.stderr)
+        return 2
     x = inputs.generate(w)
-    measure = measure_fused if args.path == "fused" else measure_unfused
-    ms = measure(torch, binding, x, args.steps, args.warmup)
-    tflops = w.flops() / (ms * 1e-3) / 1e12
-
-    traffic = None
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            t = json.load(f).get(w.name)
-        if t and t.get("path", "fused") == args.path and t.get("kernel_source_sha256") == _kernel_digest():
-            traffic = t.get("bytes_per_launch")
+    g = inputs.grad_output(w) if w.dtype == "bf16" else None
+    if args.path == "backward":
+        ms = measure_backward(torch, binding, x, g, args.steps, args.warmup)
+        tflops = w.bwd_flops() / (ms * 1e-3) / 1e12
+    else:
+        measure = measure_fused if args.path == "fused" else measure_unfused
+        ms = measure(torch, binding, x, args.steps, args.warmup)
+        tflops = w.flops() / (ms * 1e-3) / 1e12
+    traffic = load_traffic(args.traffic, args.path, w.name)
 
     line = {
-        "metric": METRIC,
+        "metric": BWD_METRIC if args.path == "backward" else METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -209,7 +282,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "scale": "1/sqrt(d)", "flops_per_step": w.flops(), "path": args.path,
+                   "scale": "1/sqrt(d)",
+                   "flops_per_step": w.bwd_flops() if args.path == "backward" else w.flops(), "path": args.path,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
@@ -217,6 +291,8 @@ def main() -> int:
     if args.path == "unfused":
         line["roofline"]["bound"] = "hbm"
         line["roofline"]["note"] = "three kernels per step; see unfused bytes in the profile summary"
+    if args.path == "backward":
+        line["roofline"]["note"] = BWD_NOTE
     if not args.no_extras and args.path == "fused":
         ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
         line["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
@@ -234,17 +310,38 @@ def main() -> int:
             others[name] = entry
             del ox
         line["workloads"] = others
+    if not args.no_extras and args.path == "fused" and g is not None:
+        bms = measure_backward(torch, binding, x, g, max(20, args.steps // 2), max(10, args.warmup // 4))
+        btf = w.bwd_flops() / (bms * 1e-3) / 1e12
+        line["backward"] = {
+            "metric": BWD_METRIC, "value": round(btf, 2), "unit": "TFLOP/s", "ms_per_step": round(bms, 5),
+            "flops_per_step": w.bwd_flops(),
+            "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic(args.traffic, "backward", w.name), "note": BWD_NOTE},
+        }
+        if not args.no_cpu_baseline:
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward(x, g)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        if args.path == "backward":
+            line["cpu_baseline"] = cpu_baseline_backward(x, g)
+        else:
+            line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def _kernel_digest() -> str:
+BWD_NOTE = ("one call = three launches (row statistics, dK/dV, dQ); achieved = nominal FLOPs "
+            "(10*N^2*d per head, halved for causal) / mean call time; the kernels execute 14*N^2*d "
+            "(the dQ kernel recomputes S and dP)")
+
+
+def _kernel_digest(path: str) -> str:
+    """sha256 over the sources the given path's kernels are built from."""
     import hashlib
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "flashattention_forward_attn_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(here)):
+    for name in sorted(KERNEL_SOURCES[path]):
         with open(os.path.join(here, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()

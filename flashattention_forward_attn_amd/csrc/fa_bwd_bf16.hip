@@ -11,13 +11,15 @@
 // Three kernels on the caller's stream:
 //   1. rows:  D_i and the base-2 log-sum-exp L2_i = L_i log2(e) (+inf for a row
 //      with no valid key, so that its P is exactly 0), into the workspace.
-//   2. dK/dV: one workgroup per 128 keys of one (batch, head), one wave per 32 keys
-//      (one wave per SIMD).  Q and dO tiles of 64 queries, with their L2 and D
-//      values, stream through LDS by direct buffer loads, double-buffered.  Per
-//      32-query chunk, lane = key:
-//        S = Q K^T and dP = dO V^T (B operands K and V held in registers),
-//        P = exp2(S c - L2), dS = P (dP - D), packed to bf16,
-//        dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing LDS reads).
+//   2. dK/dV: one workgroup per 128 keys of one (batch, head), eight waves: per
+//      32 keys a score wave and a gradient wave on one SIMD.  Q and dO tiles of 32
+//      queries, with their L2 and D values, stream through LDS by direct buffer
+//      loads issued two tiles ahead.  Per tile, lane = key:
+//        score wave:    S = Q K^T and dP = dO V^T (B operands K and V held in
+//                       registers), P = exp2(S c - L2), dS = P (dP - D), packed
+//                       to bf16 and handed over through LDS;
+//        gradient wave: one tile later, dV^T += dO^T P and dK^T += Q^T dS (A
+//                       operands by transposing LDS reads).
 //   3. dQ: one workgroup per 256 queries, one wave per 32 queries; K/V tiles stream
 //      through LDS as in the forward kernel.  Lane = query:
 //        S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
@@ -60,35 +62,49 @@ __global__ __launch_bounds__(kRowThreads) void rows_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------- 2. dK and dV
 namespace kv {
-constexpr int kWaves = 4;
+// Two roles per SIMD.  Wave p (p < 4, "score wave") and wave p + 4 ("gradient
+// wave") share a SIMD and own the same 32 keys.  The score wave holds K and V of
+// its keys as MFMA operands and turns a 32-query tile into P and dS; the
+// gradient wave holds the dK and dV accumulators and consumes that tile's P and
+// dS one iteration later.  Each wave needs only its role's registers, so two
+// fit per SIMD, and one wave's exponentials and conversions overlap the other's
+// matrix products.
+constexpr int kPairs = 4;
+constexpr int kWaves = 2 * kPairs;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kKPW = 32;                 // keys per wave
-constexpr int kBKV = kWaves * kKPW;      // 128 keys per workgroup
-constexpr int kBQ = 64;                  // queries per streamed tile
+constexpr int kKPW = 32;                 // keys per wave pair
+constexpr int kBKV = kPairs * kKPW;      // 128 keys per workgroup
+constexpr int kBQ = 32;                  // queries per streamed tile
+constexpr int kStages = 4;               // tile t+2 loads while t (scores) and t-1 (gradients) are read
 
 template <int D>
 struct Tile {
     static constexpr int kRow = D * 2;
-    static constexpr int kBytes = kBQ * kRow;              // one Q or dO tile
-    static constexpr int kStats = 3 * kBQ * 4;             // L2, D, key limit of the tile
-    static constexpr int kStage = 2 * kBytes + 1024;       // Q, dO, stats (1 KB aligned)
-    static constexpr int kBlocks = kBytes / kDmaBytes;
-    static constexpr int kPerWave = kBlocks / kWaves;
-    static_assert(kBlocks % kWaves == 0, "tile must split evenly over the waves");
-    static_assert(kStats <= 1024, "stats fit their slot");
+    static constexpr int kBytes = kBQ * kRow;                // one Q or dO tile
+    static constexpr int kStatSlot = kWave * 4;              // one 4-byte-per-lane load
+    static constexpr int kStage = 2 * kBytes + 1024;         // Q, dO, then L2, D, key limit slots
+    static constexpr int kHand = 4 * kWave * 16;             // P and dS of one pair: 2 + 2 16-byte loads
+    static constexpr int kHandOff = kStages * kStage;
+    static constexpr int kSmem = kHandOff + 2 * kPairs * kHand;
+    static constexpr int kTileBlocks = kBytes / kDmaBytes;   // loads per tensor tile
+    static constexpr int kPerWave = 2 * kTileBlocks / kWaves;
+    static_assert((2 * kTileBlocks) % kWaves == 0, "Q and dO tiles must split evenly over the waves");
+    static_assert(3 * kStatSlot <= 1024, "stats fit their slots");
 };
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
             const bf16* __restrict__ dO, const float* __restrict__ Dd, const float* __restrict__ L2,
             bf16* __restrict__ dK, bf16* __restrict__ dV, int H, int N, int nkb, float c, float scale,
             const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
+    __shared__ __attribute__((aligned(1024))) char smem[T::kSmem];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = w & (kPairs - 1);
+    const bool scorer = w < kPairs;
     const int half = lane >> 5, col = lane & 31;
 
     // Key blocks in ascending order: for causal attention the first blocks see
@@ -100,55 +116,171 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * D * 2u;
     const int k0 = kb * kBKV;
-    const int kw0 = k0 + w * kKPW;           // first key of this wave
+    const int kw0 = k0 + pair * kKPW;        // first key of this wave pair
     const int kcol = kw0 + col;               // this lane's key
 
-    // K and V rows of this lane's key, as B operands (k = 8 dims per lane half)
-    bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        if (kcol < N) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kcol * D + 16 * kk + 8 * half);
-            vf[kk] = *reinterpret_cast<const bf16x8*>(V + head + (size_t)kcol * D + 16 * kk + 8 * half);
-        } else {
-            kf[kk] = bf16x8{};
-            vf[kk] = bf16x8{};
-        }
-    }
-
-    uint32_t dma_off[T::kPerWave];
+    // Direct loads: block g = i * kWaves + w of the stage's Q tile (g < kTileBlocks)
+    // or dO tile; lane l's 16 bytes land at LDS position 16 l of the block.
+    uint32_t dma_src[T::kPerWave], dma_dst[T::kPerWave];
+    bool dma_g[T::kPerWave];
 #pragma unroll
     for (int i = 0; i < T::kPerWave; ++i) {
-        const int p = (i * kWaves + w) * kDmaBytes + 16 * lane;
+        const int g = i * kWaves + w;
+        dma_g[i] = g >= T::kTileBlocks;
+        const int blk = dma_g[i] ? g - T::kTileBlocks : g;
+        const int p = blk * kDmaBytes + 16 * lane;
         const int row = p / T::kRow, slot = (p % T::kRow) / 16;
-        dma_off[i] = (uint32_t)(row * T::kRow + 16 * (slot ^ swz<D>(row)));
+        dma_src[i] = (uint32_t)(row * T::kRow + 16 * (slot ^ swz<D>(row)));
+        dma_dst[i] = (uint32_t)(dma_g[i] ? T::kBytes : 0) + blk * kDmaBytes;
     }
     const i32x4 qdesc = dma_desc(Q + head, head_bytes), gdesc = dma_desc(dO + head, head_bytes);
     const i32x4 ldesc = dma_desc(L2 + (size_t)bh * N, (uint32_t)N * 4u);
     const i32x4 ddesc = dma_desc(Dd + (size_t)bh * N, (uint32_t)N * 4u);
     const i32x4 mdesc = dma_desc(MASK ? kv_limit + (size_t)b * N : kv_limit, MASK ? (uint32_t)N * 4u : 0u);
-    auto dma_tile = [&](int stage, int q0) {
+    auto dma_tile = [&](int stage, int q0) __attribute__((always_inline)) {
         const uint32_t base = (uint32_t)q0 * T::kRow;
         const uint32_t st = lds_addr(smem + stage * T::kStage);
 #pragma unroll
-        for (int i = 0; i < T::kPerWave; ++i) {
-            const uint32_t dst = st + (i * kWaves + w) * kDmaBytes;
-            dma16(qdesc, dst, base + dma_off[i]);
-            dma16(gdesc, dst + T::kBytes, base + dma_off[i]);
-        }
+        for (int i = 0; i < T::kPerWave; ++i) dma16(dma_g[i] ? gdesc : qdesc, st + dma_dst[i], base + dma_src[i]);
         const uint32_t soff = (uint32_t)(q0 + lane) * 4u;
         if (w == 0) dma4(ldesc, st + 2 * T::kBytes, soff);
-        if (w == 1) dma4(ddesc, st + 2 * T::kBytes + kBQ * 4, soff);
-        if (MASK && w == 2) dma4(mdesc, st + 2 * T::kBytes + 2 * kBQ * 4, soff);
+        if (w == 1) dma4(ddesc, st + 2 * T::kBytes + T::kStatSlot, soff);
+        if (MASK && w == 2) dma4(mdesc, st + 2 * T::kBytes + 2 * T::kStatSlot, soff);
     };
 
-    // LDS operand offsets.  Row-major reads (A of S = Q K^T and dP = dO V^T): query
-    // row col of a 32-query chunk, chunk 2 kk + half.  Transposing reads (A of
-    // dV^T = dO^T P and dK^T = Q^T dS): lane 16 G + j addresses query
-    // 8 hs + 4 (G / 2) + j / 4 at dims 32 d32 + 16 (G % 2) + 4 (j % 4) .. +3.
-    int koff[D / 16];
+    // Queries before this block's first key see none of its keys (causal).
+    const int q_first = CAUSAL ? k0 : 0;
+    const int ntiles = (N - q_first + kBQ - 1) / kBQ;
+    // every query of tile u precedes every key of this pair
+    auto skipped = [&](int u) __attribute__((always_inline)) {
+        return CAUSAL && q_first + u * kBQ + kBQ - 1 < kw0;
+    };
+    char* const hand0 = smem + T::kHandOff + pair * T::kHand;
+
+    const bool stat_wave = w == 0 || w == 1 || (MASK && w == 2);
+    auto wait_next = [&](bool more) __attribute__((always_inline)) {
+        if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (stat_wave) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T::kPerWave + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T::kPerWave) : "memory");
+    };
+    dma_tile(0, q_first);
+    if (ntiles > 1) dma_tile(1, q_first + kBQ);
+    wait_next(ntiles > 1);
+    __syncthreads();
+
+    if (scorer) {
+        // K and V rows of this lane's key, as B operands (k = 8 dims per lane half)
+        bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * T::kRow + 16 * ((2 * kk + half) ^ swz<D>(col));
+        for (int kk = 0; kk < D / 16; ++kk) {
+            if (kcol < N) {
+                kf[kk] = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kcol * D + 16 * kk + 8 * half);
+                vf[kk] = *reinterpret_cast<const bf16x8*>(V + head + (size_t)kcol * D + 16 * kk + 8 * half);
+            } else {
+                kf[kk] = bf16x8{};
+                vf[kk] = bf16x8{};
+            }
+        }
+        // The loads above complete here, so the loop carries no wait on the memory
+        // counter, which also counts the tile loads in flight.
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            launder(kf[kk]);
+            launder(vf[kk]);
+        }
+        // Row-major reads (A of S = Q K^T and dP = dO V^T): query row col, chunk 2 kk + half.
+        int koff[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) koff[kk] = col * T::kRow + 16 * ((2 * kk + half) ^ swz<D>(col));
+
+        int st = 0;
+        for (int t = 0; t <= ntiles; ++t) {
+            const int nst = st == kStages - 1 ? 0 : st + 1;
+            if (t + 2 < ntiles) dma_tile((st + 2) & 3, q_first + (t + 2) * kBQ);
+            if (t < ntiles && !skipped(t)) {
+                const int qc0 = q_first + t * kBQ;
+                const char* Qc = smem + st * T::kStage;
+                const char* Gc = Qc + T::kBytes;
+                const float* Ls = reinterpret_cast<const float*>(Qc + 2 * T::kBytes);
+                const float* Ds = reinterpret_cast<const float*>(Qc + 2 * T::kBytes + T::kStatSlot);
+                const int* Ms = reinterpret_cast<const int*>(Qc + 2 * T::kBytes + 2 * T::kStatSlot);
+
+                // All operand reads first, then the two product chains interleaved; the
+                // score wave's products go ahead of its partner's so that its
+                // exponentials overlap the partner's products.
+                bf16x8 qa[D / 16], ga[D / 16];
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    qa[kk] = *reinterpret_cast<const bf16x8*>(Qc + koff[kk]);
+                    ga[kk] = *reinterpret_cast<const bf16x8*>(Gc + koff[kk]);
+                }
+                f32x16 s = f32x16{}, dp = f32x16{};
+                // (the priority changes are tied to the products' operands and results
+                // so that the scheduler keeps the products between them)
+                asm volatile("s_setprio 2" : "+v"(kf[0]), "+v"(vf[0]));
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], vf[kk], dp, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 16), 0);  // products
+                asm volatile("s_setprio 0" :: "v"(s[15]), "v"(dp[15]));
+                // accumulator r holds query qc0 + 8 (r / 4) + 4 half + r % 4 of this lane's key
+                float l2r[16], ddr[16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rq = 8 * i + 4 * half;
+                    const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + rq);
+                    const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + rq);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        l2r[4 * i + e] = lv[e];
+                        ddr[4 * i + e] = dv4[e];
+                    }
+                }
+                if (MASK) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4 mv = *reinterpret_cast<const u32x4*>(Ms + 8 * i + 4 * half);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (kcol >= (int)mv[e]) s[4 * i + e] = -INFINITY;
+                    }
+                }
+                if (CAUSAL && qc0 < kw0 + kKPW - 1) {  // tile crosses this pair's diagonal
+                    const int rel = kcol - qc0 - 4 * half;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) < rel) s[r] = -INFINITY;
+                }
+
+                char* hand = hand0 + (t & 1) * kPairs * T::kHand;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    u32x4 pk, dsk;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r0 = 8 * kh + 2 * q, r1 = r0 + 1;
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -l2r[r0]));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r1], c, -l2r[r1]));
+                        pk[q] = pack_bf16x2(p0, p1);
+                        dsk[q] = pack_bf16x2(p0 * (dp[r0] - ddr[r0]), p1 * (dp[r1] - ddr[r1]));
+                    }
+                    *reinterpret_cast<u32x4*>(hand + kh * kDmaBytes + 16 * lane) = pk;
+                    *reinterpret_cast<u32x4*>(hand + (2 + kh) * kDmaBytes + 16 * lane) = dsk;
+                }
+            }
+            wait_next(t + 2 < ntiles);
+            __syncthreads();
+            st = nst;
+        }
+        return;
+    }
+
+    // Gradient wave.  Transposing reads (A of dV^T = dO^T P and dK^T = Q^T dS): lane
+    // 16 G + j addresses query 8 hs + 4 (G / 2) + j / 4 at dims
+    // 32 d32 + 16 (G % 2) + 4 (j % 4) .. +3.
     int voff[D / 32][2];
     {
         const int G4 = lane >> 4, j = lane & 15;
@@ -170,106 +302,43 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
         dkacc[i] = f32x16{};
     }
 
-    // Queries before this block's first key see none of its keys (causal).
-    const int q_first = CAUSAL ? (k0 / kBQ) * kBQ : 0;
-    const int ntiles = k0 < N ? (N - q_first + kBQ - 1) / kBQ : 0;
-
-    if (ntiles > 0) dma_tile(0, q_first);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int st = t & 1;
-        const int q0 = q_first + t * kBQ;
-        if (t + 1 < ntiles) dma_tile(st ^ 1, q0 + kBQ);
-        const char* Qs = smem + st * T::kStage;
-        const char* Gs = Qs + T::kBytes;
-        const float* Ls = reinterpret_cast<const float*>(Qs + 2 * T::kBytes);
-        const float* Ds = Ls + kBQ;
-        const int* Ms = reinterpret_cast<const int*>(Ds + kBQ);
-
+    int st = 0, pst = kStages - 1;  // stage of tile t, and of tile t - 1
+    for (int t = 0; t <= ntiles; ++t) {
+        const int nst = st == kStages - 1 ? 0 : st + 1;
+        if (t + 2 < ntiles) dma_tile((st + 2) & 3, q_first + (t + 2) * kBQ);
+        if (t > 0 && !skipped(t - 1)) {
+            const char* Qc = smem + pst * T::kStage;
+            const char* Gc = Qc + T::kBytes;
+            const char* hand = hand0 + ((t - 1) & 1) * kPairs * T::kHand;
 #pragma unroll
-        for (int ch = 0; ch < kBQ / 32; ++ch) {
-            const int qc0 = q0 + 32 * ch;
-            // every query of the chunk precedes every key of this wave
-            if (CAUSAL && qc0 + 31 < kw0) continue;
-            const char* Qc = Qs + 32 * ch * T::kRow;
-            const char* Gc = Gs + 32 * ch * T::kRow;
-
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Qc + koff[kk]), kf[kk],
-                                                            s, 0, 0, 0);
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Gc + koff[kk]), vf[kk],
-                                                             dp, 0, 0, 0);
-
-            // accumulator r holds query qc0 + 8 (r / 4) + 4 half + r % 4 of this lane's key
-            float l2r[16], ddr[16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rq = 32 * ch + 8 * i + 4 * half;
-                const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + rq);
-                const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + rq);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    l2r[4 * i + e] = lv[e];
-                    ddr[4 * i + e] = dv4[e];
-                }
-            }
-            if (MASK) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rq = 32 * ch + 8 * i + 4 * half;
-                    const u32x4 mv = *reinterpret_cast<const u32x4*>(Ms + rq);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (kcol >= (int)mv[e]) s[4 * i + e] = -INFINITY;
-                }
-            }
-            if (CAUSAL && qc0 < kw0 + 31) {  // chunk crosses this wave's diagonal
-                const int rel = kcol - qc0 - 4 * half;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) < rel) s[r] = -INFINITY;
-            }
-
-            u32x4 pk[2], dsk[2];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r0 = 8 * kh + 2 * q, r1 = r0 + 1;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -l2r[r0]));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r1], c, -l2r[r1]));
-                    pk[kh][q] = pack_bf16x2(p0, p1);
-                    dsk[kh][q] = pack_bf16x2(p0 * (dp[r0] - ddr[r0]), p1 * (dp[r1] - ddr[r1]));
-                }
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh) {
+                const u32x4 pk = *reinterpret_cast<const u32x4*>(hand + kh * kDmaBytes + 16 * lane);
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
                     const u32x2 lo = tr_read(Gc + 16 * kh * T::kRow + voff[d32][0]);
                     const u32x2 hi = tr_read(Gc + 16 * kh * T::kRow + voff[d32][1]);
                     const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
                     dvacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pk[kh]), dvacc[d32], 0, 0, 0);
+                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pk), dvacc[d32], 0, 0, 0);
                 }
+            }
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh) {
+                const u32x4 dsk = *reinterpret_cast<const u32x4*>(hand + (2 + kh) * kDmaBytes + 16 * lane);
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
                     const u32x2 lo = tr_read(Qc + 16 * kh * T::kRow + voff[d32][0]);
                     const u32x2 hi = tr_read(Qc + 16 * kh * T::kRow + voff[d32][1]);
                     const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
                     dkacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, dsk[kh]), dkacc[d32], 0, 0, 0);
+                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, dsk), dkacc[d32], 0, 0, 0);
                 }
+            }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_next(t + 2 < ntiles);
         __syncthreads();
+        pst = st;
+        st = nst;
     }
 
     // Epilogue: lane holds key kcol, dims 32 d32 + 8 g + 4 half .. +3 in registers 4 g ..
