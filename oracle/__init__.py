@@ -12,10 +12,13 @@ O = softmax(scale * Q K^T + M) V and LSE = log sum exp(scale * Q K^T + M) per
 row, M being 0 on valid keys and -inf elsewhere, a row with no valid key giving
 O = 0 and LSE = -inf; and the backward pass, the gradients dQ, dK, dV of
 sum(dO * O) for a given dO, by the chain rule through the row softmax
-(optionally with the row term D_i = <dO_i, O_i> taken from a caller's stored O).
+(optionally with the row term D_i = <dO_i, O_i> taken from a caller's stored O);
+and decode, one query per sequence over a paged key/value cache reached
+through a block table.
 
-Parity: every function here is pinned, by ``tests/test_oracle.py`` (forward)
-and ``tests/test_oracle_bwd.py`` (backward), against the pages' worked
+Parity: every function here is pinned, by ``tests/test_oracle.py`` (forward),
+``tests/test_oracle_bwd.py`` (backward) and ``tests/test_oracle_decode.py``
+(paged decode), against the pages' worked
 examples, closed forms, invariants, finite differences and brute force; none
 is "parity unpinned".
 """
@@ -65,6 +68,9 @@ def load(path: str = LIBRARY):
                                          ctypes.c_int, ctypes.c_double, ip, i64, i64,
                                          i64, lp, i64, lp, dp, dp, dp, ctypes.c_int]
     lib.fa_oracle_bwd_sample.restype = ctypes.c_int
+    lib.fa_oracle_decode_paged.argtypes = [dp, dp, dp, ip, ip, dp, dp, i64, i64, i64, i64, i64, i64,
+                                           ctypes.c_double, ctypes.c_int]
+    lib.fa_oracle_decode_paged.restype = ctypes.c_int
     return lib
 
 
@@ -214,3 +220,36 @@ def attention_bwd_sample(q, k, v, dout, b: int, h: int, q_rows, k_rows, causal: 
     if rc != 0:
         raise RuntimeError(f"fa_oracle_bwd_sample failed ({rc})")
     return dq, dk, dv
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[float] = None,
+                 nthreads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode attention over a paged cache.
+
+    q (B, H, d); k_cache, v_cache (num_pages, H, page_size, d); block_table
+    (B, max_pages) int32; seq_lens (B,) int32.  Returns (o, lse): o float64
+    (B, H, d), lse float64 (B, H), natural log.  scale defaults to 1/sqrt(d).
+    """
+    lib = lib or _library()
+    q, k_cache, v_cache = _f64(q), _f64(k_cache), _f64(v_cache)
+    if q.ndim != 3 or k_cache.ndim != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be (B, H, d) and the caches (num_pages, H, page_size, d)")
+    B, H, d = q.shape
+    num_pages, Hc, page_size, dc = k_cache.shape
+    if (Hc, dc) != (H, d):
+        raise ValueError("cache heads and head dim must match q")
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if bt.ndim != 2 or bt.shape[0] != B or lens.shape != (B,):
+        raise ValueError("block_table must be (B, max_pages) and seq_lens (B,)")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((B, H, d), np.float64)
+    lse = np.empty((B, H), np.float64)
+    rc = lib.fa_oracle_decode_paged(_ptr(q, ctypes.c_double), _ptr(k_cache, ctypes.c_double),
+                                    _ptr(v_cache, ctypes.c_double), _ptr(bt, ctypes.c_int32),
+                                    _ptr(lens, ctypes.c_int32), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                                    B, H, d, page_size, bt.shape[1], num_pages, float(scale), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_decode_paged failed ({rc})")
+    return o, lse

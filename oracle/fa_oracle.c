@@ -410,3 +410,91 @@ int fa_oracle_bwd_sample(const double *q, const double *k, const double *v, cons
     free(lse_h); free(dd_h);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Decode over a paged key/value cache.
+ *
+ * One query per sequence (N_q = 1, the token being generated), attending to
+ * every cached key of its own sequence.  The cache is cut into fixed-size
+ * pages; a per-sequence block table maps logical page p (keys p*page_size ..
+ * p*page_size + page_size - 1) to a physical page of the pool, so that a
+ * sequence's pages may lie anywhere ("CS336 第五讲 · GPU 与 GPU 优化", the
+ * PagedAttention section: pages of 16 tokens and the block table).  The
+ * result is the attention of the plain definition above over those keys:
+ *   key j of sequence b, head h, is k_cache[page, h, j % page_size, :] with
+ *   page = block_table[b, j / page_size], for 0 <= j < seq_lens[b];
+ *   s_j = scale * <q[b,h,:], key j>, m = max_j s_j, w_j = exp(s_j - m),
+ *   o[b,h,:] = sum_j w_j v_j / sum_j w_j, lse[b,h] = m + ln(sum_j w_j);
+ *   a sequence with no key gets o = 0 and lse = -inf.
+ * Layouts: q, o [B, H, d]; k_cache, v_cache [num_pages, H, page_size, d];
+ * block_table [B, max_pages]; seq_lens [B]; lse [B, H].  A length outside
+ * [0, max_pages * page_size] or a referenced page outside [0, num_pages) is
+ * an error (-1): the oracle only defines valid caches.
+ * ------------------------------------------------------------------------ */
+int fa_oracle_decode_paged(const double *q, const double *k_cache, const double *v_cache,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           double *o, double *lse,
+                           int64_t B, int64_t H, int64_t d, int64_t page_size,
+                           int64_t max_pages, int64_t num_pages, double scale, int nthreads)
+{
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return -1;
+    if (B < 0 || H < 0 || d <= 0 || page_size <= 0 || max_pages < 0 || num_pages < 0) return -1;
+    int64_t max_len = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t len = seq_lens[b];
+        if (len < 0 || len > max_pages * page_size) return -1;
+        for (int64_t p = 0; p * page_size < len; ++p) {
+            const int64_t page = block_table[b * max_pages + p];
+            if (page < 0 || page >= num_pages) return -1;
+        }
+        if (len > max_len) max_len = len;
+    }
+    int failed = 0;
+#ifdef _OPENMP
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel num_threads(nt)
+    {
+        double *s = (double *)malloc((size_t)(max_len > 0 ? max_len : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                const int64_t b = bh / H, h = bh % H, len = seq_lens[b];
+                const double *qv = q + bh * d;
+                double *ov = o + bh * d;
+                for (int64_t c = 0; c < d; ++c) ov[c] = 0.0;
+                if (len == 0) {
+                    lse[bh] = -INFINITY;
+                    continue;
+                }
+                /* scores over the sequence's keys, gathered through the block table */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < len; ++j) {
+                    const int64_t page = block_table[b * max_pages + j / page_size];
+                    const double *kj = k_cache + ((page * H + h) * page_size + j % page_size) * d;
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < d; ++c) acc += qv[c] * kj[c];
+                    s[j] = scale * acc;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < len; ++j) {
+                    const int64_t page = block_table[b * max_pages + j / page_size];
+                    const double *vj = v_cache + ((page * H + h) * page_size + j % page_size) * d;
+                    const double w = exp(s[j] - m);
+                    l += w;
+                    for (int64_t c = 0; c < d; ++c) ov[c] += w * vj[c];
+                }
+                for (int64_t c = 0; c < d; ++c) ov[c] /= l;
+                lse[bh] = m + log(l);
+            }
+            free(s);
+        }
+    }
+    return failed ? -1 : 0;
+}
