@@ -21,9 +21,14 @@ Besides the headline number the line carries:
                   workload with a seeded dO, timed the same way, with its own
                   roofline (nominal backward FLOPs 10*B*H*N^2*d, halved for
                   causal, per call / mean call time) and its own oracle
-                  baseline (the full fp64 backward of a few heads).
+                  baseline (the full fp64 backward of a few heads);
+  decode       -- decode over a paged key/value cache (fa_decode_paged_bf16: two
+                  launches) on the decode workload, HBM-bound: achieved GB/s =
+                  algorithmic bytes (keys and values of every valid position, q,
+                  o, lse, block-table entries) per call / mean call time, against
+                  8000 GB/s; its oracle baseline runs the whole workload.
 
---path backward makes the backward pass the timed step instead.
+--path backward / --path decode make that pass the timed step instead.
 """
 from __future__ import annotations
 
@@ -39,6 +44,9 @@ HEADLINE = "bf16_causal_b2h32n4096d128"
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
 BWD_METRIC = "attention bwd TFLOP/s (bf16, nominal 10*N^2*d per head) and % of MI355X MFMA peak"
+DEC_METRIC = "paged decode attention GB/s (bf16, keys and values read once) and % of MI355X HBM bandwidth"
+PEAK_HBM_GBS = 8000.0
+DECODE_HEADLINE = "decode_b64h32d128_len2048"
 
 # Sources each timed path is built from: a traffic figure measured on other
 # sources is stale and is not reported.
@@ -46,6 +54,7 @@ KERNEL_SOURCES = {
     "fused": ["fa_fwd_bf16.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
     "unfused": ["fa_unfused.hip", "fa_common.h", "fa_launch.h"],
     "backward": ["fa_bwd_bf16.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
+    "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_launch.h"],
 }
 
 
@@ -132,6 +141,67 @@ def measure_backward(torch, binding, x, g, steps, warmup):
     ms = time_launches(torch, launch, steps, warmup)
     del q, k, v, o, lse, lim, dout, dq, dk, dv, ws
     return ms
+
+
+def decode_bytes(xd) -> int:
+    """Algorithmic bytes of one paged decode call."""
+    w = xd.workload
+    pages = int(sum(-(-int(n) // inputs_page(xd)) for n in xd.seq_lens))
+    return xd.kv_bytes() + 2 * (w.B * w.H * w.d * 2) + w.B * w.H * 4 + pages * 4 + w.B * 4
+
+
+def inputs_page(xd) -> int:
+    return int(xd.k_cache.shape[2])
+
+
+def measure_decode(torch, binding, xd, steps, warmup):
+    """Mean ms per fa_decode_paged_bf16 call (split and combine launches)."""
+    w = xd.workload
+    dev16 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, kc, vc = dev16(xd.q_bits), dev16(xd.k_bits), dev16(xd.v_bits)
+    bt = torch.from_numpy(xd.block_table).cuda()
+    sl = torch.from_numpy(xd.seq_lens).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(binding.fa_decode_workspace_bytes(w.B, w.H, w.d, w.max_pages), dtype=torch.uint8,
+                     device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        binding.fa_decode_paged_bf16(q, kc, vc, bt, sl, o, lse, w.scale, ws, stream)
+
+    ms = time_launches(torch, launch, steps, warmup)
+    del q, kc, vc, bt, sl, o, lse, ws
+    return ms
+
+
+def cpu_baseline_decode(xd):
+    """The oracle's paged decode over the whole workload."""
+    import oracle
+    threads = host_threads()
+    q, kc, vc = (np.ascontiguousarray(a, dtype=np.float64) for a in (xd.q, xd.k_cache, xd.v_cache))
+    t0 = time.perf_counter()
+    oracle.decode_paged(q, kc, vc, xd.block_table, xd.seq_lens, xd.workload.scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {xd.workload.name} workload, fp64, {dt:.1f} s; same algorithmic bytes",
+            "seconds": round(dt, 3)}
+
+
+def decode_entry(torch, binding, xd, steps, warmup, traffic_file, cpu: bool):
+    ms = measure_decode(torch, binding, xd, steps, warmup)
+    gbs = decode_bytes(xd) / (ms * 1e-3) / 1e9
+    entry = {"metric": DEC_METRIC, "workload": xd.workload.name, "value": round(gbs, 1), "unit": "GB/s",
+             "ms_per_step": round(ms, 5), "bytes_per_step": decode_bytes(xd),
+             "TFLOP/s": round(xd.flops() / (ms * 1e-3) / 1e12, 2),
+             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "traffic": load_traffic(traffic_file, "decode", xd.workload.name),
+                          "note": "one call = two launches (splits, then their merge); achieved = algorithmic "
+                                  "bytes per call / mean call time"}}
+    if cpu:
+        entry["cpu_baseline"] = cpu_baseline_decode(xd)
+    return entry
 
 
 def effective_flops(x) -> float:
@@ -222,9 +292,10 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
-    ap.add_argument("--path", choices=("fused", "unfused", "backward"), default="fused",
-                    help="time the fused kernel (default), the unfused three-kernel baseline or the "
-                         "backward pass as the step")
+    ap.add_argument("--path", choices=("fused", "unfused", "backward", "decode"), default="fused",
+                    help="time the fused kernel (default), the unfused three-kernel baseline, the "
+                         "backward pass or the paged decode as the step")
+    ap.add_argument("--decode-workload", default=DECODE_HEADLINE)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
                          "its FETCH_SIZE/WRITE_SIZE calibrate the traffic counters")
@@ -252,6 +323,22 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
         return 0
     binding.load()
+
+    if args.path == "decode":
+        xd = inputs.generate_decode(inputs.DECODE_WORKLOADS[args.decode_workload])
+        entry = decode_entry(torch, binding, xd, args.steps, args.warmup, args.traffic, not args.no_cpu_baseline)
+        line = {"metric": DEC_METRIC, "value": entry["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": entry["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
+                "config": {"workload": xd.workload.name, "B": xd.workload.B, "H": xd.workload.H, "d": xd.workload.d,
+                           "max_len": xd.workload.max_len, "page": 16, "path": "decode",
+                           "bytes_per_step": entry["bytes_per_step"], "parallelism": "single GPU"},
+                "roofline": entry["roofline"]}
+        if "cpu_baseline" in entry:
+            line["cpu_baseline"] = entry["cpu_baseline"]
+        print(json.dumps(line), flush=True)
+        return 0
 
     w = inputs.WORKLOADS[args.workload]
     if w.dtype != "bf16" and args.path == "backward":
@@ -322,6 +409,10 @@ def main() -> int:
         }
         if not args.no_cpu_baseline:
             line["backward"]["cpu_baseline"] = cpu_baseline_backward(x, g)
+        xd = inputs.generate_decode(inputs.DECODE_WORKLOADS[args.decode_workload])
+        line["decode"] = decode_entry(torch, binding, xd, max(20, args.steps // 2), max(10, args.warmup // 4),
+                                      args.traffic, not args.no_cpu_baseline)
+        del xd
     if not args.no_cpu_baseline:
         if args.path == "backward":
             line["cpu_baseline"] = cpu_baseline_backward(x, g)

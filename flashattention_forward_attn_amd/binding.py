@@ -51,6 +51,10 @@ def load(path: str = LIBRARY):
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, vp]
     lib.fa_bwd_bf16.restype = ctypes.c_int
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_paged_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode_paged_bf16.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -152,6 +156,42 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: Optio
     ws = torch.empty(fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=q.device)
     fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, causal, scale, kv_limit, ws, stream)
     return dq, dk, dv
+
+
+def fa_decode_workspace_bytes(B: int, H: int, d: int, max_pages: int) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, d, max_pages))
+
+
+def fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: float, workspace=None,
+                         stream=None) -> None:
+    """Decode over a paged cache: q, o bf16 [B, H, d]; k_cache, v_cache bf16 [num_pages, H, 16, d];
+    block_table int32 [B, max_pages]; seq_lens int32 [B]; lse fp32 [B, H]; workspace a device uint8
+    tensor of at least fa_decode_workspace_bytes(B, H, d, max_pages) bytes."""
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [B, H, d], the caches [num_pages, H, page_size, d], block_table [B, max_pages]")
+    B, H, d = (int(x) for x in q.shape)
+    num_pages, _, page_size, _ = (int(x) for x in k_cache.shape)
+    max_pages = int(block_table.shape[1])
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().fa_decode_paged_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                       _ptr(o), _ptr(lse), B, H, d, page_size, max_pages, num_pages, float(scale),
+                                       _ptr(workspace), nbytes, _stream(stream)))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[float] = None, stream=None):
+    """Allocate o, lse and the workspace with torch and run the paged decode (bf16).  Returns (o, lse)."""
+    import torch
+    B, H, d = (int(x) for x in q.shape)
+    if scale is None:
+        scale = d ** -0.5
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"the paged decode takes bf16 tensors, got {q.dtype}")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa_decode_workspace_bytes(B, H, d, int(block_table.shape[1]))), dtype=torch.uint8,
+                     device=q.device)
+    fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale, ws, stream)
+    return o, lse
 
 
 def attention(q, k, v, causal: bool = False, scale: Optional[float] = None, kv_limit=None, unfused: bool = False,

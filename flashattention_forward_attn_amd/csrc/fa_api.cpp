@@ -94,6 +94,11 @@ size_t bwd_workspace_bytes(int B, int H, int N) {
     return (size_t)(2 * fa::bwd_stats_floats(B, H, N) * 4);
 }
 
+size_t decode_workspace_bytes(int B, int H, int d, int max_pages) {
+    if (B < 1 || H < 1 || max_pages < 1 || (d != 64 && d != 128)) return 0;
+    return (size_t)fa::decode_workspace_floats(B, H, d, max_pages) * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,6 +168,40 @@ fa_status fa_bwd_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
     return hip_status(fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal != 0, scale,
                                           kv_limit, static_cast<float*>(workspace),
                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages) {
+    return decode_workspace_bytes(B, H, d, max_pages);
+}
+
+fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf16* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens, fa_bf16* o, float* lse, int B,
+                               int H, int d, int page_size, int max_pages, int num_pages, float scale,
+                               void* workspace, size_t workspace_bytes_given, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage)
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const size_t need = decode_workspace_bytes(B, H, d, max_pages);
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, kWsAlign)) return FA_ERR_WORKSPACE;
+    const int64_t row_bytes = (int64_t)B * H * d * 2;
+    const int64_t cache_bytes = (int64_t)num_pages * H * fa::kDecodePage * d * 2;
+    const Range ins[] = {span(q, row_bytes), span(k_cache, cache_bytes), span(v_cache, cache_bytes),
+                         span(block_table, (int64_t)B * max_pages * 4), span(seq_lens, (int64_t)B * 4)};
+    const Range outs[] = {span(o, row_bytes), span(lse, (int64_t)B * H * 4), span(workspace, (int64_t)need)};
+    for (int i = 0; i < 3; ++i) {
+        for (Range in : ins)
+            if (overlap(outs[i], in)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+    }
+    return hip_status(fa::launch_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, max_pages,
+                                             num_pages, scale, static_cast<float*>(workspace),
+                                             static_cast<hipStream_t>(stream)));
 }
 
 const char* fa_status_str(fa_status s) {

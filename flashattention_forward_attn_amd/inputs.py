@@ -197,3 +197,93 @@ def grad_output(w: Workload, seed: Optional[int] = None) -> GradOutput:
     if w.dtype == "f32":
         return GradOutput(g, None)
     raise ValueError(f"unknown dtype {w.dtype!r}")
+
+
+# ---------------------------------------------------------------- paged decode
+#
+# Decode: one query per sequence over its cached keys, the cache cut into pages
+# of 16 tokens reached through a per-sequence block table.  Draw order from
+# ``numpy.random.default_rng([seed, 2])``: the sequence lengths (uniform in
+# [1, max_len]), the permutation that scatters the needed pages (plus a spare
+# tenth) over the pool, q, then k_cache and v_cache (float32 standard normal
+# draws over the whole pool, 256 pages per draw, unused slots included), all
+# rounded to bf16.
+# Block-table entries past a sequence's pages point at page 0.
+
+DECODE_PAGE = 16
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    d: int
+    max_len: int        # tokens reserved per sequence (max_pages * 16)
+    seed: int = 0
+
+    @property
+    def max_pages(self) -> int:
+        return -(-self.max_len // DECODE_PAGE)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    workload: DecodeWorkload
+    q: np.ndarray            # float32 (B, H, d), bf16 values
+    k_cache: np.ndarray      # float32 (num_pages, H, 16, d), bf16 values
+    v_cache: np.ndarray
+    block_table: np.ndarray  # int32 (B, max_pages)
+    seq_lens: np.ndarray     # int32 (B,)
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    def kv_bytes(self) -> int:
+        """Bytes of the cached keys and values the sequences actually use (bf16)."""
+        return int(self.seq_lens.astype(np.int64).sum()) * self.workload.H * self.workload.d * 2 * 2
+
+    def flops(self) -> float:
+        """Two length x d products per (sequence, head)."""
+        return 4.0 * float(self.seq_lens.astype(np.int64).sum()) * self.workload.H * self.workload.d
+
+
+# Decode workloads: the page's scenario (space reserved for 2048 tokens per
+# sequence, each sequence at its own length), and a long-context variant.
+DECODE_WORKLOADS = {
+    "decode_b64h32d128_len2048": DecodeWorkload("decode_b64h32d128_len2048", 64, 32, 128, 2048),
+    "decode_b8h16d64_len16384": DecodeWorkload("decode_b8h16d64_len16384", 8, 16, 64, 16384),
+}
+
+
+def generate_decode(w: DecodeWorkload, seed: Optional[int] = None, lens=None) -> DecodeInputs:
+    rng = np.random.default_rng([w.seed if seed is None else seed, 2])
+    drawn = rng.integers(1, w.max_len + 1, size=w.B).astype(np.int32)
+    seq_lens = drawn if lens is None else np.asarray(lens, np.int32)
+    need = [-(-max(int(n), 0) // DECODE_PAGE) for n in seq_lens]
+    total = sum(need)
+    num_pages = max(1, total + total // 10)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    block_table = np.zeros((w.B, w.max_pages), np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        block_table[b, :n] = perm[at:at + n]
+        at += n
+    qb = bf16_bits(rng.standard_normal((w.B, w.H, w.d), dtype=np.float32))
+    cache_bits = []
+    for _ in range(2):  # k_cache, then v_cache, drawn 256 pages at a time
+        bits = np.empty((num_pages, w.H, DECODE_PAGE, w.d), np.uint16)
+        for p0 in range(0, num_pages, 256):
+            n = min(256, num_pages - p0)
+            bits[p0:p0 + n] = bf16_bits(rng.standard_normal((n, w.H, DECODE_PAGE, w.d), dtype=np.float32))
+        cache_bits.append(bits)
+    kb, vb = cache_bits
+    return DecodeInputs(w, bf16_to_f32(qb), bf16_to_f32(kb), bf16_to_f32(vb), block_table, seq_lens, qb, kb, vb)

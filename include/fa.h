@@ -1,6 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so): the
- * forward pass (fused and unfused) and the backward pass of the fused forward.
+ * forward pass (fused and unfused), the backward pass of the fused forward, and
+ * decode attention over a paged key/value cache.
  *
  * The operation.  For every batch item b, head h and query row i:
  *
@@ -166,6 +167,57 @@ fa_status fa_bwd_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
                       int B, int H, int N, int d, int causal, float scale,
                       const int32_t *kv_limit,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace fa_decode_paged_bf16 needs: per sequence, head and 64-key
+ * split an unnormalised fp32 output row (d values) and its (max, sum) pair, with
+ * max_pages * 16 / 64 splits (rounded up) per sequence.  Returns 0 if an argument
+ * is out of range.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages);
+
+/*
+ * Decode attention over a paged key/value cache: one query per sequence (the
+ * token being generated) attends to every cached key of its sequence.
+ *
+ *   key j of sequence b, head h (0 <= j < seq_lens[b]) is
+ *     k_cache[page, h, j % 16, :] with page = block_table[b * max_pages + j / 16],
+ *   o[b,h,:]  = sum_j softmax_j( scale * <q[b,h,:], key j> ) * value j
+ *   lse[b,h]  = log sum_j exp( scale * <q[b,h,:], key j> )   (natural log)
+ *
+ * and a sequence with no key gets o = 0 and lse = -inf.  The cache is cut into
+ * pages of 16 tokens, and the block table maps a sequence's logical pages to
+ * physical pages anywhere in the pool ("CS336 第五讲 · GPU 与 GPU 优化", the
+ * PagedAttention section).  The key range of each sequence is split into pieces
+ * of 64 keys processed in parallel and merged with the online-softmax rescaling
+ * ("FlashAttention 1–4 ...", sections "FlashAttention (v1)" and
+ * "FlashAttention-2").
+ *
+ * Layout.  q, o: contiguous [B, H, d] bf16.  k_cache, v_cache: contiguous
+ * [num_pages, H, 16, d] bf16 (one page of one head is 16 * d contiguous values).
+ * block_table: contiguous [B, max_pages] int32.  seq_lens: [B] int32.  lse:
+ * [B, H] fp32.  page_size must be 16; d in {64, 128}; B, H in [1, 65535];
+ * max_pages, num_pages >= 1.
+ *
+ * Contents.  Lengths are clamped to [0, max_pages * 16].  Block-table entries of
+ * pages past a sequence's length are never read; an entry inside the length that
+ * lies outside [0, num_pages) is not dereferenced, and its 16 keys and values read
+ * as zeros.  Cache slots past a sequence's length in its last page may hold
+ * anything.
+ *
+ * Memory: every pointer is caller-owned device memory; q, k_cache, v_cache, o
+ * 16-byte aligned, block_table, seq_lens, lse 4-byte aligned; workspace at least
+ * fa_decode_workspace_bytes(B, H, d, max_pages) bytes, 256-byte aligned,
+ * overwritten.  o, lse and the workspace must not overlap an input or each other.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (B, H, max_pages, num_pages or page_size out of
+ * range), FA_ERR_HEAD_DIM, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_WORKSPACE,
+ * FA_ERR_ALIAS, FA_ERR_HIP, as for the forward.
+ */
+fa_status fa_decode_paged_bf16(const fa_bf16 *q, const fa_bf16 *k_cache, const fa_bf16 *v_cache,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               fa_bf16 *o, float *lse,
+                               int B, int H, int d, int page_size, int max_pages, int num_pages,
+                               float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status s);

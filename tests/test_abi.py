@@ -144,3 +144,49 @@ def test_backward_workspace_bytes(lib):
     assert f(1, 1, 65) == 2 * 128 * 4
     assert f(2, 32, 4096) == 2 * 2 * 32 * 4096 * 4
     assert f(0, 1, 1) == 0 and f(1, 1, 0) == 0
+
+
+# paged decode: fake addresses past the ones above
+QD, KC, VC, BT, SL, OD, LD, WD = (0x10000000 * (i + 20) for i in range(8))
+
+
+def dec(lib, q=QD, kc=KC, vc=VC, bt=BT, sl=SL, o=OD, l=LD, ws=WD, ws_bytes=None, B=2, H=3, d=128, page=16,
+        max_pages=8, num_pages=20, scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_bytes(B, H, d, max_pages)
+    return lib.fa_decode_paged_bf16(q, kc, vc, bt, sl, o, l, B, H, d, page, max_pages, num_pages, scale, ws,
+                                    ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    assert dec(lib, q=None) == 1
+    assert dec(lib, bt=None) == 1
+    assert dec(lib, sl=None) == 1
+    assert dec(lib, l=None) == 1
+    assert dec(lib, B=0) == 2
+    assert dec(lib, H=70000) == 2
+    assert dec(lib, page=32) == 2              # pages of 16 tokens only
+    assert dec(lib, max_pages=0) == 2
+    assert dec(lib, num_pages=0) == 2
+    assert dec(lib, d=96) == 3
+    assert dec(lib, scale=0.0) == 4
+    assert dec(lib, kc=KC + 8) == 5
+    assert dec(lib, o=OD + 2) == 5
+    assert dec(lib, bt=BT + 2) == 5
+    assert dec(lib, ws=None) == 6
+    assert dec(lib, ws_bytes=64) == 6
+    assert dec(lib, ws=WD + 128) == 6
+    assert dec(lib, o=KC + 4096) == 8          # output inside the key cache
+    assert dec(lib, l=BT) == 8                 # lse over the block table
+    assert dec(lib, ws=OD) == 8                # workspace over the output
+    assert dec(lib, l=OD + 16) == 8            # lse over the output
+
+
+def test_decode_workspace_bytes(lib):
+    f = lib.fa_decode_workspace_bytes
+    # per (sequence, head, 64-key split): d floats, then a (max, sum) pair; each part padded to 64 floats
+    assert f(1, 1, 128, 4) == (128 + 64) * 4              # 4 pages = one split
+    assert f(1, 1, 128, 5) == (2 * 128 + 64) * 4          # 5 pages = two splits
+    assert f(2, 32, 128, 128) == (2 * 32 * 32 * 128 + 2 * 32 * 32 * 2) * 4
+    assert f(1, 1, 64, 1) == (64 + 64) * 4
+    assert f(0, 1, 128, 1) == 0 and f(1, 1, 96, 1) == 0 and f(1, 1, 128, 0) == 0
