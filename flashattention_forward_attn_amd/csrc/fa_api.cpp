@@ -179,7 +179,8 @@ fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const f
                                int H, int d, int page_size, int max_pages, int num_pages, float scale,
                                void* workspace, size_t workspace_bytes_given, void* stream) {
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
-    if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage)
+    if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage ||
+        fa::decode_max_splits(max_pages) > 65535)
         return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;

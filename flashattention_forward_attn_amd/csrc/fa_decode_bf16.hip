@@ -16,13 +16,15 @@
 // wide coalesced loads with many bytes in flight.
 //
 // Two kernels on the caller's stream:
-//   1. split: one wave per (sequence, head, 64-key split).  D/8 lanes per key,
-//      each loading 16 bytes, so one load instruction covers 512/D consecutive
-//      keys of one page (a page of one head is 16 * D * 2 contiguous bytes).
-//      Scores by packed bf16 dot products, summed within each lane group by DPP;
-//      the wave's max, exponentials, sum and weighted value rows are written as
-//      an unnormalised partial (m, l, o) in base 2.
-//   2. combine: one wave per (sequence, head) merges its splits:
+//   1. split: one workgroup per (sequence, head, 256-key split), one wave per 64
+//      keys; the grid runs over (sequence, head) fastest and splits slowest.  D/8 lanes per key, each loading 16 bytes, so one load instruction
+//      covers 512/D consecutive keys of one page (a page of one head is
+//      16 * D * 2 contiguous bytes).  Scores by packed bf16 dot products, summed
+//      within each lane group by DPP; each wave's max, exponentials, sum and
+//      weighted value rows form a partial (m, l, o) in base 2, and the four
+//      waves' partials are merged through LDS into one unnormalised partial per
+//      split.
+//   2. combine: one workgroup per (sequence, head) merges its splits:
 //      m = max m_s, l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l.
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -31,9 +33,10 @@ namespace fa {
 namespace decode {
 
 constexpr int kPage = kDecodePage;            // tokens per page
-constexpr int kSplitKeys = kDecodeSplitKeys;  // keys per split (one wave)
-constexpr int kSplitWaves = 4;                // splits per workgroup
-constexpr int kThreads = kSplitWaves * kWave;
+constexpr int kSplitKeys = kDecodeSplitKeys;  // keys per split (one workgroup)
+constexpr int kWaves = 4;
+constexpr int kWaveKeys = kSplitKeys / kWaves;  // keys per wave
+constexpr int kThreads = kWaves * kWave;
 
 // Sum over aligned groups of W lanes (W = 8 or 16); every lane of a group gets
 // the group's sum.  Quad swaps, then half-row and row mirrors (within a group
@@ -79,36 +82,40 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const bf16* __restrict_
                                                          float c) {
     constexpr int LPK = D / 8;           // lanes per key
     constexpr int KPI = kWave / LPK;     // keys per load instruction
-    constexpr int NI = kSplitKeys / KPI; // load instructions per split
+    constexpr int NI = kWaveKeys / KPI;  // load instructions per wave
     static_assert(kPage % KPI == 0, "a load instruction stays inside one page");
+    __shared__ float sh_ml[2 * kWaves];
+    __shared__ __attribute__((aligned(16))) float sh_o[kWaves * D];
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int split = blockIdx.x * kSplitWaves + w;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int split = blockIdx.y;
+    const int key0 = split * kSplitKeys + w * kWaveKeys;  // this wave's first key
+
+    // Physical pages of this wave's keys, read next to the length (the entries
+    // stay inside the table row; they are used only below the length).
+    constexpr int kPagesPerWave = kWaveKeys / kPage;
+    int page[kPagesPerWave];
+#pragma unroll
+    for (int p = 0; p < kPagesPerWave; ++p) {
+        const int lp = key0 / kPage + p;
+        page[p] = lp < max_pages ? block_table[(size_t)b * max_pages + lp] : -1;
+    }
     const int len = clamp_len(seq_lens[b], max_pages);
-    const int key0 = split * kSplitKeys;
-    if (split >= max_splits || key0 >= len) return;
+    if (split >= max_splits || split * kSplitKeys >= len) return;  // the whole workgroup
+    const bool active = key0 < len;
 
     const int grp = lane / LPK, cidx = lane % LPK;  // key within an instruction, 8-dim chunk
     const size_t bh = (size_t)b * H + h;
     const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + bh * D + 8 * cidx);
-
-    // Physical pages of this split (uniform); pages past the length are not read.
-    constexpr int kPagesPerSplit = kSplitKeys / kPage;
-    int page[kPagesPerSplit];
-#pragma unroll
-    for (int p = 0; p < kPagesPerSplit; ++p) {
-        const int lp = key0 / kPage + p;
-        page[p] = lp * kPage < len ? block_table[(size_t)b * max_pages + lp] : -1;
-    }
 
     bf16x8 kr[NI], vr[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int pg = page[(i * KPI) / kPage];
         const int slot = (i * KPI) % kPage + grp;
-        if (pg >= 0 && pg < num_pages) {
+        if (active && (key0 + i * KPI) < len && pg >= 0 && pg < num_pages) {
             const size_t off = (((size_t)pg * H + h) * kPage + slot) * D + 8 * cidx;
             kr[i] = *reinterpret_cast<const bf16x8*>(kc + off);
             vr[i] = *reinterpret_cast<const bf16x8*>(vc + off);
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const bf16* __restrict_
         s[i] = key < len ? acc * c : -INFINITY;
         m = fmaxf(m, s[i]);
     }
-    m = cross_max<LPK>(m);  // key0 < len, so m is finite
+    m = cross_max<LPK>(m);  // -inf only for a wave past the length
 
     float l = 0.f, o[8];
 #pragma unroll
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const bf16* __restrict_
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int key = key0 + i * KPI + grp;
-        const float p = __builtin_amdgcn_exp2f(s[i] - m);
+        const float p = active ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
         l += p;
         if (key < len) {  // slots past the length may hold anything
             const u32x4 va = __builtin_bit_cast(u32x4, vr[i]);
@@ -160,57 +167,99 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const bf16* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = cross_sum<LPK>(o[e]);
 
-    const size_t part = bh * max_splits + split;
+    // merge the four waves' partials (a wave past the length has m = -inf, l = 0, o = 0)
     if (grp == 0) {
-        f32x4* dst = reinterpret_cast<f32x4*>(part_o + part * D + 8 * cidx);
+        f32x4* dst = reinterpret_cast<f32x4*>(sh_o + w * D + 8 * cidx);
         dst[0] = f32x4{o[0], o[1], o[2], o[3]};
         dst[1] = f32x4{o[4], o[5], o[6], o[7]};
     }
     if (lane == 0) {
-        part_ml[2 * part] = m;
-        part_ml[2 * part + 1] = l;
+        sh_ml[2 * w] = m;
+        sh_ml[2 * w + 1] = l;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float mm = sh_ml[0];
+#pragma unroll
+        for (int v = 1; v < kWaves; ++v) mm = fmaxf(mm, sh_ml[2 * v]);  // wave 0 is below the length
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float a = __builtin_amdgcn_exp2f(sh_ml[2 * v] - mm);
+            acc = fmaf(a, sh_o[v * D + tid], acc);
+            lsum = fmaf(a, sh_ml[2 * v + 1], lsum);
+        }
+        const size_t part = bh * max_splits + split;
+        part_o[part * D + tid] = acc;
+        if (tid == 0) {
+            part_ml[2 * part] = mm;
+            part_ml[2 * part + 1] = lsum;
+        }
     }
 }
 
-// One wave per (sequence, head): lane owns dims lane * D / 64 ...
+// One workgroup per (sequence, head): thread t adds up dim t % D over the
+// splits s = t / D (mod 256 / D), the groups are then summed through LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            const int32_t* __restrict__ seq_lens, bf16* __restrict__ o,
-                                                           float* __restrict__ lse, int B, int H, int max_pages,
+                                                           float* __restrict__ lse, int H, int max_pages,
                                                            int max_splits) {
-    constexpr int E = D / kWave;  // dims per lane: 2 or 1
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long bh = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
-    if (bh >= (long long)B * H) return;
+    constexpr int G = kThreads / D;  // split groups
+    constexpr int U = 4;             // splits in flight per thread
+    __shared__ float sh_m[kWaves];
+    __shared__ float sh_acc[kThreads], sh_l[G];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+    const size_t bh = blockIdx.x;
     const int b = (int)(bh / H);
     const int len = clamp_len(seq_lens[b], max_pages);
     const int n = (len + kSplitKeys - 1) / kSplitKeys;
-    bf16* orow = o + bh * D + E * lane;
     if (n == 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) orow[e] = (bf16)0.f;
-        if (lane == 0) lse[bh] = -INFINITY;
+        if (tid < D) o[bh * D + tid] = (bf16)0.f;
+        if (tid == 0) lse[bh] = -INFINITY;
         return;
     }
     const float* ml = part_ml + 2 * bh * max_splits;
-    const float* po = part_o + bh * max_splits * D + E * lane;
+    const float* po = part_o + bh * max_splits * D;
     float m = -INFINITY;
-    for (int s = lane; s < n; s += kWave) m = fmaxf(m, ml[2 * s]);
+    for (int s = tid; s < n; s += kThreads) m = fmaxf(m, ml[2 * s]);
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    float l = 0.f, acc[E];
+    if (lane == 0) sh_m[w] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
+
+    const int dim = tid % D, g = tid / D;
+    float acc = 0.f, l = 0.f;
+    for (int s0 = g; s0 < n; s0 += G * U) {
+        float a[U], x[U], y[U];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int s = 0; s < n; ++s) {
-        const float a = __builtin_amdgcn_exp2f(ml[2 * s] - m);
-        l = fmaf(a, ml[2 * s + 1], l);
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * G;
+            a[u] = s < n ? ml[2 * s] : -INFINITY;
+            y[u] = s < n ? ml[2 * s + 1] : 0.f;
+            x[u] = s < n ? po[(size_t)s * D + dim] : 0.f;
+        }
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(a, po[(size_t)s * D + e], acc[e]);
+        for (int u = 0; u < U; ++u) {
+            const float f = __builtin_amdgcn_exp2f(a[u] - m);
+            acc = fmaf(f, x[u], acc);
+            l = fmaf(f, y[u], l);
+        }
     }
-    const float inv = 1.f / l;
+    sh_acc[tid] = acc;
+    if (dim == 0) sh_l[g] = l;
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f, lt = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) orow[e] = (bf16)(acc[e] * inv);
-    if (lane == 0) lse[bh] = (m + __log2f(l)) * kLn2;
+        for (int v = 0; v < G; ++v) {
+            t += sh_acc[v * D + tid];
+            lt += sh_l[v];
+        }
+        o[bh * D + tid] = (bf16)(t / lt);
+        if (tid == 0) lse[bh] = (m + __log2f(lt)) * kLn2;
+    }
 }
 
 }  // namespace decode
@@ -222,9 +271,11 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
     float* part_o = workspace;
     float* part_ml = workspace + decode_part_o_floats(B, H, d, max_pages);
     const float c = scale * kLog2e;
-    const dim3 grid_split((unsigned)((max_splits + decode::kSplitWaves - 1) / decode::kSplitWaves), (unsigned)H,
-                          (unsigned)B);
-    const unsigned grid_combine = (unsigned)(((long long)B * H + decode::kSplitWaves - 1) / decode::kSplitWaves);
+    // (sequence, head) fastest, splits slowest: the first splits, present for
+    // every sequence, go out first, and the grid's empty tail (splits past short
+    // sequences) comes last.  Measured 243 -> 192 us on ragged lengths.
+    const dim3 grid_split((unsigned)((long long)B * H), (unsigned)max_splits);
+    const unsigned grid_combine = (unsigned)((long long)B * H);
     const bf16* Q = static_cast<const bf16*>(q);
     const bf16* K = static_cast<const bf16*>(k_cache);
     const bf16* V = static_cast<const bf16*>(v_cache);
@@ -241,10 +292,10 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
     }
     if (d == 128)
         hipLaunchKernelGGL((decode::combine_kernel<128>), dim3(grid_combine), dim3(decode::kThreads), 0, stream,
-                           part_o, part_ml, seq_lens, O, lse, B, H, max_pages, max_splits);
+                           part_o, part_ml, seq_lens, O, lse, H, max_pages, max_splits);
     else
         hipLaunchKernelGGL((decode::combine_kernel<64>), dim3(grid_combine), dim3(decode::kThreads), 0, stream,
-                           part_o, part_ml, seq_lens, O, lse, B, H, max_pages, max_splits);
+                           part_o, part_ml, seq_lens, O, lse, H, max_pages, max_splits);
     return hipGetLastError();
 }
 

@@ -35,11 +35,11 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float scale, const int32_t* kv_limit, float* workspace, hipStream_t stream);
 
 // Decode over a paged cache: pages of kDecodePage tokens; the key range of a
-// sequence is split into pieces of kDecodeSplitKeys keys.  The workspace holds
-// the splits' unnormalised outputs (fp32 [B*H*max_splits, d], padded to 64
+// sequence is split into pieces of kDecodeSplitKeys keys (one workgroup each).
+// The workspace holds the splits' unnormalised outputs (fp32 [B*H*max_splits, d], padded to 64
 // floats) and then their (max, sum) pairs (fp32 [B*H*max_splits, 2]).
 constexpr int kDecodePage = 16;
-constexpr int kDecodeSplitKeys = 64;
+constexpr int kDecodeSplitKeys = 256;
 inline int64_t decode_max_splits(int max_pages) {
     return ((int64_t)max_pages * kDecodePage + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
 }

@@ -169,9 +169,9 @@ fa_status fa_bwd_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of workspace fa_decode_paged_bf16 needs: per sequence, head and 64-key
+ * Bytes of workspace fa_decode_paged_bf16 needs: per sequence, head and 256-key
  * split an unnormalised fp32 output row (d values) and its (max, sum) pair, with
- * max_pages * 16 / 64 splits (rounded up) per sequence.  Returns 0 if an argument
+ * max_pages * 16 / 256 splits (rounded up) per sequence.  Returns 0 if an argument
  * is out of range.
  */
 size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages);
@@ -189,7 +189,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages);
  * pages of 16 tokens, and the block table maps a sequence's logical pages to
  * physical pages anywhere in the pool ("CS336 第五讲 · GPU 与 GPU 优化", the
  * PagedAttention section).  The key range of each sequence is split into pieces
- * of 64 keys processed in parallel and merged with the online-softmax rescaling
+ * of 256 keys processed in parallel and merged with the online-softmax rescaling
  * ("FlashAttention 1–4 ...", sections "FlashAttention (v1)" and
  * "FlashAttention-2").
  *
@@ -197,7 +197,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages);
  * [num_pages, H, 16, d] bf16 (one page of one head is 16 * d contiguous values).
  * block_table: contiguous [B, max_pages] int32.  seq_lens: [B] int32.  lse:
  * [B, H] fp32.  page_size must be 16; d in {64, 128}; B, H in [1, 65535];
- * max_pages, num_pages >= 1.
+ * max_pages in [1, 1048560] (at most 65535 splits of 256 keys); num_pages >= 1.
  *
  * Contents.  Lengths are clamped to [0, max_pages * 16].  Block-table entries of
  * pages past a sequence's length are never read; an entry inside the length that

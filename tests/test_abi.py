@@ -168,6 +168,7 @@ def test_decode_validation(lib):
     assert dec(lib, page=32) == 2              # pages of 16 tokens only
     assert dec(lib, max_pages=0) == 2
     assert dec(lib, num_pages=0) == 2
+    assert dec(lib, max_pages=65535 * 16 + 1) == 2   # more than 65535 splits
     assert dec(lib, d=96) == 3
     assert dec(lib, scale=0.0) == 4
     assert dec(lib, kc=KC + 8) == 5
@@ -184,9 +185,9 @@ def test_decode_validation(lib):
 
 def test_decode_workspace_bytes(lib):
     f = lib.fa_decode_workspace_bytes
-    # per (sequence, head, 64-key split): d floats, then a (max, sum) pair; each part padded to 64 floats
-    assert f(1, 1, 128, 4) == (128 + 64) * 4              # 4 pages = one split
-    assert f(1, 1, 128, 5) == (2 * 128 + 64) * 4          # 5 pages = two splits
-    assert f(2, 32, 128, 128) == (2 * 32 * 32 * 128 + 2 * 32 * 32 * 2) * 4
+    # per (sequence, head, 256-key split): d floats, then a (max, sum) pair; each part padded to 64 floats
+    assert f(1, 1, 128, 16) == (128 + 64) * 4             # 16 pages = one split
+    assert f(1, 1, 128, 17) == (2 * 128 + 64) * 4         # 17 pages = two splits
+    assert f(2, 32, 128, 128) == (2 * 32 * 8 * 128 + 2 * 32 * 8 * 2) * 4
     assert f(1, 1, 64, 1) == (64 + 64) * 4
     assert f(0, 1, 128, 1) == 0 and f(1, 1, 96, 1) == 0 and f(1, 1, 128, 0) == 0
