@@ -184,7 +184,7 @@ def cpu_baseline_decode(xd):
     oracle.decode_paged(q, kc, vc, xd.block_table, xd.seq_lens, xd.workload.scale, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {xd.workload.name} workload, fp64, {dt:.1f} s; same algorithmic bytes",
+            "sample": f"the whole {xd.workload.name} workload, fp64, {dt:.3f} s; same algorithmic bytes",
             "seconds": round(dt, 3)}
 
 
