@@ -13,12 +13,14 @@ row, M being 0 on valid keys and -inf elsewhere, a row with no valid key giving
 O = 0 and LSE = -inf; and the backward pass, the gradients dQ, dK, dV of
 sum(dO * O) for a given dO, by the chain rule through the row softmax
 (optionally with the row term D_i = <dO_i, O_i> taken from a caller's stored O);
-and decode, one query per sequence over a paged key/value cache reached
-through a block table.
+decode, one query per sequence over a paged key/value cache reached through a
+block table; and the FP8 forward: Q and K rotated by random signs and a
+Hadamard transform, encoded to E4M3 with one power-of-two scale per tile, then
+attention on the dequantised values.
 
 Parity: every function here is pinned, by ``tests/test_oracle.py`` (forward),
-``tests/test_oracle_bwd.py`` (backward) and ``tests/test_oracle_decode.py``
-(paged decode), against the pages' worked
+``tests/test_oracle_bwd.py`` (backward), ``tests/test_oracle_decode.py``
+(paged decode) and ``tests/test_oracle_fp8.py`` (FP8), against the pages' worked
 examples, closed forms, invariants, finite differences and brute force; none
 is "parity unpinned".
 """
@@ -71,6 +73,15 @@ def load(path: str = LIBRARY):
     lib.fa_oracle_decode_paged.argtypes = [dp, dp, dp, ip, ip, dp, dp, i64, i64, i64, i64, i64, i64,
                                            ctypes.c_double, ctypes.c_int]
     lib.fa_oracle_decode_paged.restype = ctypes.c_int
+    bp = ctypes.POINTER(ctypes.c_uint8)
+    sp = ctypes.POINTER(ctypes.c_int8)
+    lib.fa_oracle_fp8_quantize.argtypes = [dp, sp, ctypes.c_int, bp, ip, i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.fa_oracle_fp8_quantize.restype = ctypes.c_int
+    lib.fa_oracle_fwd_fp8.argtypes = [bp, ip, i64, bp, ip, i64, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_double, ip, ctypes.c_int]
+    lib.fa_oracle_fwd_fp8.restype = ctypes.c_int
+    lib.fa_oracle_fp8_rotate.argtypes = [dp, sp, ctypes.POINTER(ctypes.c_float), i64, i64]
+    lib.fa_oracle_fp8_rotate.restype = ctypes.c_int
     return lib
 
 
@@ -253,3 +264,86 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[flo
     if rc != 0:
         raise RuntimeError(f"fa_oracle_decode_paged failed ({rc})")
     return o, lse
+
+
+def fp8_quantize(x, signs=None, tile_rows: int = 64, nthreads: int = 0, lib=None):
+    """E4M3 codes of x (B, H, N, d) with one power-of-two scale per tile of rows.
+
+    With signs (length d, entries +-1) each row is first rotated by the
+    unnormalised Hadamard transform of (signs * row); without, rows are encoded
+    as they are.  Returns (codes uint8 (B, H, N, d), exps int32 (B, H, ceil(N / tile_rows))).
+    """
+    lib = lib or _library()
+    x = _f64(x)
+    B, H, N, d = x.shape
+    sg = None if signs is None else np.ascontiguousarray(signs, dtype=np.int8)
+    if sg is not None and sg.shape != (d,):
+        raise ValueError("signs must have length d")
+    codes = np.empty((B, H, N, d), np.uint8)
+    exps = np.empty((B, H, -(-N // tile_rows)), np.int32)
+    rc = lib.fa_oracle_fp8_quantize(_ptr(x, ctypes.c_double), None if sg is None else _ptr(sg, ctypes.c_int8),
+                                    int(sg is not None), _ptr(codes, ctypes.c_uint8), _ptr(exps, ctypes.c_int32),
+                                    B, H, N, d, int(tile_rows), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fp8_quantize failed ({rc})")
+    return codes, exps
+
+
+def attention_fp8(qc, qe, q_tile: int, kc, ke, k_tile: int, v, causal: bool = False, scale: Optional[float] = None,
+                  rotated: bool = True, kv_limit=None, nthreads: int = 0, lib=None):
+    """Attention on E4M3-coded q and k (codes and per-tile exponents from fp8_quantize) and v.
+
+    rotated: the codes are of Hadamard-rotated rows, so scores are divided by d.
+    Returns (o, lse) as fp64 arrays, like attention().
+    """
+    lib = lib or _library()
+    qc = np.ascontiguousarray(qc, dtype=np.uint8)
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    qe = np.ascontiguousarray(qe, dtype=np.int32)
+    ke = np.ascontiguousarray(ke, dtype=np.int32)
+    v = _f64(v)
+    B, H, N, d = qc.shape
+    if kc.shape != qc.shape or v.shape != qc.shape:
+        raise ValueError("q, k, v must share one (B, H, N, d) shape")
+    if qe.shape != (B, H, -(-N // q_tile)) or ke.shape != (B, H, -(-N // k_tile)):
+        raise ValueError("exponent arrays do not match the tiles")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lim, lim_p = _limits(kv_limit, B, N)
+    o = np.empty((B, H, N, d), np.float64)
+    lse = np.empty((B, H, N), np.float64)
+    rc = lib.fa_oracle_fwd_fp8(_ptr(qc, ctypes.c_uint8), _ptr(qe, ctypes.c_int32), int(q_tile),
+                               _ptr(kc, ctypes.c_uint8), _ptr(ke, ctypes.c_int32), int(k_tile),
+                               _ptr(v, ctypes.c_double), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                               B, H, N, d, int(bool(causal)), float(scale), float(d if rotated else 1), lim_p,
+                               int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd_fp8 failed ({rc})")
+    return o, lse
+
+
+def e4m3_values() -> np.ndarray:
+    """fp64 value of every E4M3 code 0..255 (NaN for the two NaN codes), from the format definition."""
+    out = np.empty(256)
+    for code in range(256):
+        s, E, m = code >> 7, (code >> 3) & 15, code & 7
+        if (code & 0x7F) == 0x7F:
+            out[code] = np.nan
+            continue
+        v = m * 2.0 ** -9 if E == 0 else (1 + m / 8) * 2.0 ** (E - 7)
+        out[code] = -v if s else v
+    return out
+
+
+def fp8_rotate(x, signs, lib=None) -> np.ndarray:
+    """The rotation alone: float32 H (signs * row) for every row of x (..., d)."""
+    lib = lib or _library()
+    x = _f64(x)
+    d = x.shape[-1]
+    sg = np.ascontiguousarray(signs, dtype=np.int8)
+    y = np.empty(x.shape, np.float32)
+    rc = lib.fa_oracle_fp8_rotate(_ptr(x, ctypes.c_double), _ptr(sg, ctypes.c_int8), _ptr(y, ctypes.c_float),
+                                  x.size // d, d)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fp8_rotate failed ({rc})")
+    return y

@@ -498,3 +498,178 @@ int fa_oracle_decode_paged(const double *q, const double *k_cache, const double 
     }
     return failed ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------
+ * FP8 forward: quantisation of Q and K, and attention on the quantised values.
+ *
+ * "FlashAttention 1–4 ...", section "FlashAttention-3" (FP8 with block
+ * quantization and incoherent processing): one FP8 scale per tile of rows
+ * instead of one per tensor, and Q and K both multiplied by the same random
+ * orthogonal matrix before quantising -- random sign flips followed by a
+ * Hadamard transform, O(d log d) per row -- which leaves Q K^T unchanged while
+ * spreading an outlier over every coordinate.
+ *
+ * The encoding, step by step (the plainest reading where the page is silent):
+ *   1. rotate each row x (length d, a power of two) of Q or K:
+ *        y = H (s * x)   with s[c] in {+1, -1} given by the caller and H the
+ *        unnormalised Sylvester-Hadamard matrix (entries +-1, H H^T = d I),
+ *        computed in fp32 as the butterfly: for h = 1, 2, 4, ..., d/2, every
+ *        pair (i, i + h) with i & h == 0 becomes (y_i + y_{i+h}, y_i - y_{i+h});
+ *   2. per tile of `tile_rows` consecutive rows of one head (the last tile may
+ *      be short), amax = max |y| and the exponent e = the smallest integer with
+ *      amax <= 448 * 2^e (448 is the largest E4M3 value), clamped to
+ *      [-127, 127]; e = 0 for an all-zero tile;
+ *   3. code = E4M3(y * 2^-e), rounding to nearest, ties to even.
+ * E4M3 (OCP FP8): 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; subnormals m * 2^-9; largest value 448.
+ * Since (H s q) . (H s k) = d (q . k), attention on the quantised values uses
+ *   s_ij = (scale / d) * sum_c deq(q_i)_c deq(k_j)_c,  deq(code) = E4M3 value * 2^e,
+ * and otherwise the plain definition above (V unchanged).
+ * ------------------------------------------------------------------------ */
+
+/* E4M3 value of a code (codes 0x7F and 0xFF, the NaNs, are never produced). */
+static double e4m3_value(uint8_t code)
+{
+    const int s = code >> 7, E = (code >> 3) & 15, m = code & 7;
+    const double v = E == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, E - 7);
+    return s ? -v : v;
+}
+
+/* E4M3 code of x, |x| <= 448: nearest representable value, ties to the even code. */
+static uint8_t e4m3_encode(float x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;                    /* a in [2^E, 2^(E+1)) */
+    if (E < -6) E = -6;               /* subnormals share the step of the lowest binade */
+    const double step = ldexp(1.0, E - 3);
+    const double r = nearbyint(a / step);   /* exact quotient; current mode rounds ties to even */
+    const double v = r * step;
+    if (v == 0.0) return sign;
+    int e2;
+    frexp(v, &e2);
+    const int E2 = e2 - 1;
+    if (E2 < -6) return sign | (uint8_t)(int)(v / ldexp(1.0, -9));
+    const int mant = (int)(v / ldexp(1.0, E2 - 3)) - 8;
+    return sign | (uint8_t)(((E2 + 7) << 3) | mant);
+}
+
+/* Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax == 0. */
+static int tile_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int k;
+    const double m = frexp((double)amax, &k);   /* amax = m 2^k, m in [0.5, 1); 448 = 0.875 2^9 */
+    int e = (m <= 0.875) ? k - 9 : k - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* One row: y = H (s * x) in fp32, butterfly stages h = 1, 2, ..., d/2. */
+static void rotate_row(const double *x, const int8_t *signs, int64_t d, float *y)
+{
+    for (int64_t c = 0; c < d; ++c) y[c] = (float)x[c] * (float)signs[c];
+    for (int64_t h = 1; h < d; h <<= 1)
+        for (int64_t i = 0; i < d; ++i) {
+            if (i & h) continue;
+            const float a = y[i], b = y[i + h];
+            y[i] = a + b;
+            y[i + h] = a - b;
+        }
+}
+
+/* Quantise x [B, H, N, d] (exact bf16 values as fp64): codes [B, H, N, d],
+ * exps [B, H, ceil(N / tile_rows)].  rotate = 0 skips step 1 (for the
+ * per-tensor baseline below).  Returns 0 or -1. */
+int fa_oracle_fp8_quantize(const double *x, const int8_t *signs, int rotate,
+                           uint8_t *codes, int32_t *exps,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int64_t tile_rows, int nthreads)
+{
+    if (!x || !codes || !exps || (rotate && !signs) || B < 0 || H < 0 || N < 0 || tile_rows <= 0) return -1;
+    if (d <= 0 || (d & (d - 1))) return -1;
+    const int64_t nt = (N + tile_rows - 1) / tile_rows;
+    int failed = 0;
+#ifdef _OPENMP
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel num_threads(nth)
+    {
+        float *y = (float *)malloc((size_t)(tile_rows * d) * sizeof(float));
+        if (!y) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < B * H * nt; ++t) {
+                const int64_t bh = t / nt, tile = t % nt;
+                const int64_t r0 = tile * tile_rows;
+                const int64_t nr = (r0 + tile_rows <= N) ? tile_rows : N - r0;
+                float amax = 0.0f;
+                for (int64_t r = 0; r < nr; ++r) {
+                    const double *xr = x + (bh * N + r0 + r) * d;
+                    float *yr = y + r * d;
+                    if (rotate) {
+                        rotate_row(xr, signs, d, yr);
+                    } else {
+                        for (int64_t c = 0; c < d; ++c) yr[c] = (float)xr[c];
+                    }
+                    for (int64_t c = 0; c < d; ++c) {
+                        const float a = fabsf(yr[c]);
+                        if (a > amax) amax = a;
+                    }
+                }
+                const int e = tile_exponent(amax);
+                exps[t] = e;
+                const float inv = (float)ldexp(1.0, -e);   /* exact power of two */
+                for (int64_t r = 0; r < nr; ++r)
+                    for (int64_t c = 0; c < d; ++c)
+                        codes[(bh * N + r0 + r) * d + c] = e4m3_encode(y[r * d + c] * inv);
+            }
+            free(y);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* Attention on quantised q and k (codes with per-tile exponents as produced
+ * above: q tiles of q_tile rows, k tiles of k_tile rows) and fp64 v.  With
+ * score_div = d for rotated inputs (1 for unrotated ones).  o [B, H, N, d],
+ * lse [B, H, N].  Masks as in fa_oracle_fwd.  Returns 0 or -1. */
+int fa_oracle_fwd_fp8(const uint8_t *qc, const int32_t *qe, int64_t q_tile,
+                      const uint8_t *kc, const int32_t *ke, int64_t k_tile,
+                      const double *v, double *o, double *lse,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int causal, double scale, double score_div, const int32_t *kv_limit, int nthreads)
+{
+    if (!qc || !qe || !kc || !ke || !v || !o || !lse || B < 0 || H < 0 || N < 0 || d <= 0) return -1;
+    if (q_tile <= 0 || k_tile <= 0 || !(score_div > 0.0)) return -1;
+    const int64_t nqt = (N + q_tile - 1) / q_tile, nkt = (N + k_tile - 1) / k_tile;
+    double *qd = (double *)malloc((size_t)(B * H * N * d > 0 ? B * H * N * d : 1) * sizeof(double));
+    double *kd = (double *)malloc((size_t)(B * H * N * d > 0 ? B * H * N * d : 1) * sizeof(double));
+    if (!qd || !kd) { free(qd); free(kd); return -1; }
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t r = 0; r < N; ++r)
+            for (int64_t c = 0; c < d; ++c) {
+                const int64_t i = (bh * N + r) * d + c;
+                qd[i] = ldexp(e4m3_value(qc[i]), qe[bh * nqt + r / q_tile]);
+                kd[i] = ldexp(e4m3_value(kc[i]), ke[bh * nkt + r / k_tile]);
+            }
+    const int rc = fa_oracle_fwd(qd, kd, v, o, lse, B, H, N, d, causal, scale / score_div, kv_limit, nthreads);
+    free(qd);
+    free(kd);
+    return rc;
+}
+
+/* The rotation of step 1 alone, for checking: y [rows, d] = H (s * x) in fp32. */
+int fa_oracle_fp8_rotate(const double *x, const int8_t *signs, float *y, int64_t rows, int64_t d)
+{
+    if (!x || !signs || !y || rows < 0 || d <= 0 || (d & (d - 1))) return -1;
+    for (int64_t r = 0; r < rows; ++r) rotate_row(x + r * d, signs, d, y + r * d);
+    return 0;
+}
