@@ -55,6 +55,10 @@ def load(path: str = LIBRARY):
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_paged_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_decode_paged_bf16.restype = ctypes.c_int
+    lib.fa_fp8_quantize_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa_fp8_quantize_bf16.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -191,6 +195,49 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[flo
     ws = torch.empty(max(1, fa_decode_workspace_bytes(B, H, d, int(block_table.shape[1]))), dtype=torch.uint8,
                      device=q.device)
     fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale, ws, stream)
+    return o, lse
+
+
+FP8_Q_TILE, FP8_K_TILE = 32, 64
+
+
+def fa_fp8_quantize_bf16(x, signs, codes, exps, tile_rows: int, stream=None) -> None:
+    """Rotate (signs, Hadamard) and encode a bf16 [B, H, N, d] tensor: codes uint8 [B, H, N, d],
+    exps int32 [B, H, ceil(N / tile_rows)]; tile_rows 32 for q, 64 for k."""
+    B, H, N, d = _dims(x)
+    _check(load().fa_fp8_quantize_bf16(_ptr(x), _ptr(signs), _ptr(codes), _ptr(exps), B, H, N, d, int(tile_rows),
+                                       _stream(stream)))
+
+
+def fa_fwd_fp8(q_codes, q_exps, k_codes, k_exps, v, o, lse, causal: bool, scale: float, kv_limit=None,
+               stream=None) -> None:
+    """Fused forward on E4M3 q and k codes (from fa_fp8_quantize_bf16) and bf16 v."""
+    B, H, N, d = _dims(v)
+    _check(load().fa_fwd_fp8(_ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v), _ptr(o), _ptr(lse),
+                             B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit), _stream(stream)))
+
+
+def fp8_quantize(x, signs, tile_rows: int, stream=None):
+    """Allocate and fill (codes, exps) for a bf16 tensor."""
+    import torch
+    B, H, N, d = _dims(x)
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    exps = torch.empty((B, H, -(-N // tile_rows)), dtype=torch.int32, device=x.device)
+    fa_fp8_quantize_bf16(x, signs, codes, exps, tile_rows, stream)
+    return codes, exps
+
+
+def attention_fp8(q, k, v, signs, causal: bool = False, scale: Optional[float] = None, kv_limit=None, stream=None):
+    """FP8 forward from bf16 q, k, v: quantise q and k (same signs), then attention.  Returns (o, lse)."""
+    import torch
+    B, H, N, d = _dims(q)
+    if scale is None:
+        scale = d ** -0.5
+    qc, qe = fp8_quantize(q, signs, FP8_Q_TILE, stream)
+    kc, ke = fp8_quantize(k, signs, FP8_K_TILE, stream)
+    o = torch.empty_like(v)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(qc, qe, kc, ke, v, o, lse, causal, scale, kv_limit, stream)
     return o, lse
 
 

@@ -205,11 +205,54 @@ fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const f
                                              static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fp8_quantize_bf16(const fa_bf16* x, const int8_t* signs, uint8_t* codes, int32_t* exps, int B, int H,
+                               int N, int d, int tile_rows, void* stream) {
+    if (!x || !signs || !codes || !exps) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || (tile_rows != fa::kFp8QTile && tile_rows != fa::kFp8KTile)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    const int64_t elems = (int64_t)B * H * N * d;
+    if (elems > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(exps, 4)) return FA_ERR_ALIGN;
+    const int64_t ntile = (int64_t)B * H * ((N + tile_rows - 1) / tile_rows);
+    const Range ins[] = {span(x, elems * 2), span(signs, d)};
+    const Range outs[] = {span(codes, elems), span(exps, ntile * 4)};
+    for (Range out : outs)
+        for (Range in : ins)
+            if (overlap(out, in)) return FA_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return FA_ERR_ALIAS;
+    return hip_status(fa::launch_fp8_quantize(x, signs, codes, exps, B, H, N, d, tile_rows,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8(const uint8_t* q_codes, const int32_t* q_exps, const uint8_t* k_codes, const int32_t* k_exps,
+                     const fa_bf16* v, fa_bf16* o, float* lse, int B, int H, int N, int d, int causal, float scale,
+                     const int32_t* kv_limit, void* stream) {
+    if (!q_codes || !q_exps || !k_codes || !k_exps || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    const int64_t elems = (int64_t)B * H * N * d;
+    if (elems > INT32_MAX) return FA_ERR_SHAPE;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(q_exps, 4) ||
+        !aligned(k_exps, 4) || !aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4)))
+        return FA_ERR_ALIGN;
+    const int64_t nqt = (int64_t)B * H * ((N + fa::kFp8QTile - 1) / fa::kFp8QTile);
+    const int64_t nkt = (int64_t)B * H * ((N + fa::kFp8KTile - 1) / fa::kFp8KTile);
+    const Range ins[] = {span(q_codes, elems), span(k_codes, elems), span(q_exps, nqt * 4), span(k_exps, nkt * 4),
+                         span(v, elems * 2), span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0)};
+    const Range ro = span(o, elems * 2), rl = span(lse, (int64_t)B * H * N * 4);
+    for (Range in : ins)
+        if (overlap(ro, in) || overlap(rl, in)) return FA_ERR_ALIAS;
+    if (overlap(ro, rl)) return FA_ERR_ALIAS;
+    return hip_status(fa::launch_fused_fp8(q_codes, q_exps, k_codes, k_exps, v, o, lse, B, H, N, d, causal != 0,
+                                           scale, kv_limit, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_str(fa_status s) {
     switch (s) {
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
-        case FA_ERR_SHAPE: return "B, H or N out of range";
+        case FA_ERR_SHAPE: return "a size (B, H, N, pages, tile rows) is out of range";
         case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
         case FA_ERR_SCALE: return "scale must be finite and positive";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse and kv_limit 4-byte aligned";

@@ -1,0 +1,421 @@
+// fa_fwd_fp8.hip -- FP8 variant of the fused forward for gfx950: Q and K in E4M3
+// with one power-of-two scale per tile, after incoherent processing.
+//
+// The method ("FlashAttention 1–4: How IO-Awareness Reshaped the Attention
+// Kernel", section "FlashAttention-3", FP8 with block quantization and
+// incoherent processing): Q and K are multiplied by the same random orthogonal
+// matrix -- random sign flips, then a Hadamard transform, O(d log d) per row --
+// which leaves Q K^T unchanged but spreads an outlier over every coordinate;
+// each tile of rows then gets its own FP8 scale, so an outlier only costs its
+// own tile resolution.
+//
+// Two kernels:
+//   1. quantise: one workgroup per tile of 32 (Q) or 64 (K) rows of one head;
+//      d/8 lanes per row, 8 values per lane.  y = H (s * x) in fp32 by the
+//      butterfly (stages h = 1, 2, 4 inside a lane, then across lanes), the
+//      tile's max |y|, the smallest exponent e with max |y| <= 448 * 2^e, and
+//      codes E4M3(y * 2^-e) by v_cvt_pk_fp8_f32 (round to nearest even).  H is
+//      the unnormalised Sylvester matrix (entries +-1), so scores carry a
+//      factor d, removed in the softmax scale.
+//   2. attention: the bf16 kernel's structure (8 waves x 32 query rows, K/V
+//      tiles of 64 keys by direct-to-LDS loads, transposed scores, bf16 P V)
+//      with S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands,
+//      and the two tiles' exponents passed as its E8M0 block scales, so the
+//      product comes out already scaled.  V stays bf16.
+#include "fa_common.h"
+#include "fa_launch.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace fp8 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- 1. quantise
+constexpr int kQuantThreads = 256;
+
+// Smallest e with a <= 448 * 2^e (a = m 2^k, m in [0.5, 1), 448 = 0.875 2^9),
+// clamped to [-127, 127]; 0 for a == 0.  Exact integer logic on the bits.
+__device__ __forceinline__ int tile_exponent(float a) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, a);
+    const int E = (int)((u >> 23) & 0xff);
+    const uint32_t M = u & 0x7fffffu;
+    if (E == 0) return M == 0 ? 0 : -127;  // subnormal maxima need e below -127
+    int e = (E - 126) - 9 + (M > 0x600000u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <int D, int T>
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __restrict__ x,
+                                                              const int8_t* __restrict__ signs,
+                                                              uint8_t* __restrict__ codes, int32_t* __restrict__ exps,
+                                                              int N, int nt) {
+    constexpr int LPR = D / 8;                  // lanes per row
+    constexpr int RPP = kQuantThreads / LPR;    // rows per pass
+    constexpr int PASSES = (T + RPP - 1) / RPP;
+    static_assert(T % RPP == 0 || RPP % T == 0, "tile and pass shapes");
+    __shared__ float wmax[kQuantThreads / kWave];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const long long bh = blockIdx.x / nt;
+    const int tile = blockIdx.x % nt;
+    const int rp = tid / LPR, cidx = tid % LPR;
+
+    float sg[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = (float)signs[8 * cidx + e];
+
+    float y[PASSES][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rin = p * RPP + rp, row = tile * T + rin;
+        const bool ok = rin < T && row < N;
+        bf16x8 v = bf16x8{};
+        if (ok) v = *reinterpret_cast<const bf16x8*>(x + (bh * N + row) * D + 8 * cidx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[p][e] = (float)v[e] * sg[e];
+        // butterfly stages inside the lane: dims 8 cidx + i, pairs (i, i + h)
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (!(i & h)) {
+                    const float a = y[p][i], b = y[p][i + h];
+                    y[p][i] = a + b;
+                    y[p][i + h] = a - b;
+                }
+        // stages across the row's lanes: h = 8 hb; the lane holding the lower dim adds
+#pragma unroll
+        for (int hb = 1; hb < LPR; hb <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float other = __shfl_xor(y[p][i], hb, kWave);
+                y[p][i] = (cidx & hb) ? other - y[p][i] : y[p][i] + other;
+            }
+        if (ok)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[p][i]));
+    }
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    if (lane == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kQuantThreads / kWave; ++i) amax = fmaxf(amax, wmax[i]);
+    const int e = tile_exponent(amax);
+    const float inv = __builtin_ldexpf(1.f, -e);  // exact power of two
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rin = p * RPP + rp, row = tile * T + rin;
+        if (rin < T && row < N) {
+            u32x2 out;
+            uint32_t w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[p][0] * inv, y[p][1] * inv, 0, false);
+            w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[p][2] * inv, y[p][3] * inv, (int)w0, true);
+            uint32_t w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[p][4] * inv, y[p][5] * inv, 0, false);
+            w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[p][6] * inv, y[p][7] * inv, (int)w1, true);
+            out.x = w0;
+            out.y = w1;
+            *reinterpret_cast<u32x2*>(codes + (bh * N + row) * D + 8 * cidx) = out;
+        }
+    }
+    if (tid == 0) exps[bh * nt + tile] = e;
+}
+
+// ---------------------------------------------------------------- 2. attention
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;  // 512
+constexpr int kQPW = kFp8QTile;           // query rows per wave = one Q tile
+constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
+constexpr int kBK = kFp8KTile;            // keys per K/V tile = one K tile
+constexpr float kStaleMax = 8.0f;         // log2 units
+
+// K rows of D E4M3 bytes: chunk c of row r sits in slot c ^ kswz(r), so that
+// 16 consecutive rows reading one chunk touch 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+    if constexpr (D == 128) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+}
+
+template <int D>
+struct Tile {
+    static constexpr int kRowK = D;                 // E4M3 key row
+    static constexpr int kRowV = 2 * D;             // bf16 value row
+    static constexpr int kBytesK = kBK * kRowK;
+    static constexpr int kBytesV = kBK * kRowV;
+    static constexpr int kStage = kBytesK + kBytesV;
+    static constexpr int kBlocksK = kBytesK / kDmaBytes;
+    static constexpr int kBlocksV = kBytesV / kDmaBytes;
+    static constexpr int kPerWaveK = (kBlocksK + kWaves - 1) / kWaves;
+    static constexpr int kPerWaveV = (kBlocksV + kWaves - 1) / kWaves;
+};
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, const uint8_t* __restrict__ Kc,
+                const int32_t* __restrict__ Ke, const bf16* __restrict__ V, bf16* __restrict__ O,
+                float* __restrict__ LSE, int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
+    __shared__ int block_max[kWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, col = lane & 31;
+
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int BHn = G / nqb;
+    int qb = bid / BHn;
+    const int bh = bid - qb * BHn;
+    if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first over the whole grid
+    const int b = bh / H;
+    const int nqt = (N + kQPW - 1) / kQPW, nkt = (N + kBK - 1) / kBK;
+
+    // Direct-to-LDS loads: block i * kWaves + w of the K tile and of the V tile.
+    uint32_t koffd[T::kPerWaveK], voffd[T::kPerWaveV];
+#pragma unroll
+    for (int i = 0; i < T::kPerWaveK; ++i) {
+        const int p = (i * kWaves + w) * kDmaBytes + 16 * lane;
+        const int row = p / T::kRowK, slot = (p % T::kRowK) / 16;
+        koffd[i] = (uint32_t)(row * T::kRowK + 16 * (slot ^ kswz<D>(row)));
+    }
+#pragma unroll
+    for (int i = 0; i < T::kPerWaveV; ++i) {
+        const int p = (i * kWaves + w) * kDmaBytes + 16 * lane;
+        const int row = p / T::kRowV, slot = (p % T::kRowV) / 16;
+        voffd[i] = (uint32_t)(row * T::kRowV + 16 * (slot ^ swz<D>(row)));
+    }
+    const i32x4 kdesc = dma_desc(Kc + (size_t)bh * N * D, (uint32_t)N * D);
+    const i32x4 vdesc = dma_desc(V + (size_t)bh * N * D, (uint32_t)N * D * 2u);
+    auto dma_tile = [&](int stage, int kv0) __attribute__((always_inline)) {
+        const uint32_t st = lds_addr(smem + stage * T::kStage);
+#pragma unroll
+        for (int i = 0; i < T::kPerWaveK; ++i)
+            if (i * kWaves + w < T::kBlocksK)
+                dma16(kdesc, st + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowK + koffd[i]);
+#pragma unroll
+        for (int i = 0; i < T::kPerWaveV; ++i)
+            if (i * kWaves + w < T::kBlocksV)
+                dma16(vdesc, st + T::kBytesK + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowV + voffd[i]);
+    };
+
+    const int q0 = qb * kBQ;
+    const int qrow = q0 + w * kQPW + col;
+    const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
+    const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
+    if (lane == 0) block_max[w] = wmax;
+
+    // Q codes of this lane's query: 32 bytes per 64 dims (k = 32 half .. +31)
+    i32x8 qf[D / 64];
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+        if (qrow < N) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(Qc + ((size_t)bh * N + qrow) * D + 64 * kk + 32 * half);
+            const u32x4 lo = src[0], hi = src[1];
+            qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+            qf[kk] = i32x8{};
+        }
+    }
+    // E8M0 block scale of this wave's Q tile (uniform)
+    const int wq = q0 / kQPW + w;
+    const int qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
+    int kv_end = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
+    const int ntiles = (kv_end + kBK - 1) / kBK;
+
+    // K (A of S^T = K Q^T): key col (+32 per slab), bytes 64 kk + 32 half .. +31,
+    // i.e. chunks 4 kk + 2 half and 4 kk + 2 half + 1 of the key row.
+    int koff[D / 64][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) koff[kk][j] = col * T::kRowK + 16 * ((4 * kk + 2 * half + j) ^ kswz<D>(col));
+    // V (A of O^T += V^T P^T) through ds_read_b64_tr_b16, as in the bf16 kernel.
+    int voff[D / 32][2];
+    {
+        const int G4 = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int key = 8 * hs + 4 * (G4 >> 1) + (j >> 2);
+#pragma unroll
+            for (int d32 = 0; d32 < D / 32; ++d32) {
+                const int dim = 32 * d32 + 16 * (G4 & 1) + 4 * (j & 3);
+                voff[d32][hs] = T::kBytesK + key * T::kRowV + 16 * ((dim >> 3) ^ swz<D>(key)) + 2 * (dim & 7);
+            }
+        }
+    }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+    float m_ref = -INFINITY, l_sum = 0.f;
+    const int32_t* kexp = Ke + (size_t)bh * nkt;
+
+    if (ntiles > 0) dma_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
+        constexpr int st = decltype(stage_c)::value;
+        if (t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
+        const char* Sb = smem + st * T::kStage;
+        const int kv0 = t * kBK;
+
+        if (kv0 < wmax) {
+            const int kscale = 127 + kexp[t];
+            f32x16 s[2];
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+                    const char* kb = Sb + sub * 32 * T::kRowK;
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + koff[kk][0]);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + koff[kk][1]);
+                    const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0, kscale, 0,
+                                                                              qscale);
+                }
+            if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (key >= lim) s[sub][r] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+            mx = halves_max(mx);
+            const float mt = mx * c;
+            if (__any(mt > m_ref + kStaleMax)) {
+                const float m_new = fmaxf(m_ref, mt);
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_sum *= alpha;
+#pragma unroll
+                for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
+                m_ref = m_new;
+            }
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+
+            u32x4 pk[4];
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int sub = ks >> 1, base = (ks & 1) * 8;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float x0 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p], c, -m_use));
+                    const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
+                    const uint32_t wv = pack_bf16x2(x0, x1);
+                    pk[ks][p] = wv;
+                    l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int d32 = 0; d32 < D / 32; ++d32) {
+                    const char* vb = Sb + 16 * ks * T::kRowV;
+                    const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
+                    const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                    oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                        __builtin_bit_cast(bf16x8, pk[ks]),
+                                                                        oacc[d32], 0, 0, 0);
+                }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+
+    const float l_tot = halves_sum(l_sum);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < N) {
+        bf16* orow = O + ((size_t)bh * N + qrow) * D;
+#pragma unroll
+        for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dim = 32 * d32 + 8 * g + 4 * half;
+                u32x2 out;
+                out.x = pack_bf16x2(oacc[d32][4 * g + 0] * inv, oacc[d32][4 * g + 1] * inv);
+                out.y = pack_bf16x2(oacc[d32][4 * g + 2] * inv, oacc[d32][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + dim) = out;
+            }
+        if (half == 0)
+            LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const bf16* v, bf16* o,
+                  float* lse, int B, int H, int N, float c, const int32_t* kv_limit, hipStream_t stream) {
+    const int nqb = (N + kBQ - 1) / kBQ;
+    const dim3 grid((unsigned)((long long)B * H * nqb));
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), 0, stream, qc, qe, kc, ke, v, o, lse, H, N,
+                       nqb, c, kv_limit);
+    return hipGetLastError();
+}
+
+}  // namespace fp8
+
+hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* codes, int32_t* exps, int B, int H, int N,
+                               int d, int tile_rows, hipStream_t stream) {
+    const bf16* X = static_cast<const bf16*>(x);
+    const int nt = (N + tile_rows - 1) / tile_rows;
+    const dim3 grid((unsigned)((long long)B * H * nt));
+#define FA_QUANT(DD, TT)                                                                                    \
+    if (d == DD && tile_rows == TT) {                                                                       \
+        hipLaunchKernelGGL((fp8::quant_kernel<DD, TT>), grid, dim3(fp8::kQuantThreads), 0, stream, X, signs, \
+                           codes, exps, N, nt);                                                             \
+        return hipGetLastError();                                                                           \
+    }
+    FA_QUANT(64, kFp8QTile)
+    FA_QUANT(64, kFp8KTile)
+    FA_QUANT(128, kFp8QTile)
+    FA_QUANT(128, kFp8KTile)
+#undef FA_QUANT
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const void* v,
+                            void* o, float* lse, int B, int H, int N, int d, bool causal, float scale,
+                            const int32_t* kv_limit, hipStream_t stream) {
+    using namespace fp8;
+    const bf16* Vb = static_cast<const bf16*>(v);
+    bf16* Ob = static_cast<bf16*>(o);
+    const float c = scale * kLog2e / (float)d;  // the rotation multiplies every score by d
+    const bool mask = kv_limit != nullptr;
+#define FA_DISPATCH(DD, CC, MM)                                                                               \
+    if (d == DD && causal == CC && mask == MM)                                                                \
+        return launch<DD, CC, MM>(qc, qe, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream);
+    FA_DISPATCH(64, false, false)
+    FA_DISPATCH(64, false, true)
+    FA_DISPATCH(64, true, false)
+    FA_DISPATCH(64, true, true)
+    FA_DISPATCH(128, false, false)
+    FA_DISPATCH(128, false, true)
+    FA_DISPATCH(128, true, false)
+    FA_DISPATCH(128, true, true)
+#undef FA_DISPATCH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -55,4 +55,19 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
                               const int32_t* seq_lens, void* o, float* lse, int B, int H, int d, int max_pages,
                               int num_pages, float scale, float* workspace, hipStream_t stream);
 
+// FP8 forward: Q codes come in tiles of kFp8QTile rows, K codes in tiles of
+// kFp8KTile rows, one int32 exponent per tile ([B, H, ceil(N / tile)]).
+constexpr int kFp8QTile = 32;
+constexpr int kFp8KTile = 64;
+
+// Rotate (random signs, Hadamard) and encode rows of a bf16 [B, H, N, d] tensor
+// to E4M3 codes [B, H, N, d] with per-tile exponents.
+hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* codes, int32_t* exps, int B, int H, int N,
+                               int d, int tile_rows, hipStream_t stream);
+
+// Fused forward with E4M3 Q and K codes (scores divided by d) and bf16 V.
+hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const void* v,
+                            void* o, float* lse, int B, int H, int N, int d, bool causal, float scale,
+                            const int32_t* kv_limit, hipStream_t stream);
+
 }  // namespace fa

@@ -287,3 +287,22 @@ def generate_decode(w: DecodeWorkload, seed: Optional[int] = None, lens=None) ->
         cache_bits.append(bits)
     kb, vb = cache_bits
     return DecodeInputs(w, bf16_to_f32(qb), bf16_to_f32(kb), bf16_to_f32(vb), block_table, seq_lens, qb, kb, vb)
+
+
+def fp8_signs(d: int, seed: int = 0) -> np.ndarray:
+    """The random +-1 vector of the FP8 path's incoherent processing (one per head
+    dimension, shared by Q and K): ``default_rng([seed, 3])``."""
+    return np.random.default_rng([seed, 3]).choice(np.array([-1, 1], np.int8), size=d)
+
+
+def outlier_qkv(B: int, H: int, N: int, d: int, seed: int = 0, n_out: int = 4, mult: float = 20.0):
+    """bf16-exact Q, K, V with a few outlier feature columns in Q and K (the FP8
+    accuracy workload): normal draws times 0.25, the chosen columns times mult."""
+    rng = np.random.default_rng([seed, 4])
+    q, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    cols = rng.choice(d, n_out, replace=False)
+    q[..., cols] *= mult
+    k[..., cols] *= mult
+    q *= 0.25
+    k *= 0.25
+    return tuple(bf16_to_f32(bf16_bits(a)) for a in (q, k, v))

@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so): the
- * forward pass (fused and unfused), the backward pass of the fused forward, and
- * decode attention over a paged key/value cache.
+ * forward pass (fused and unfused; bf16, fp32, and FP8 Q/K), the backward pass of
+ * the fused forward, and decode attention over a paged key/value cache.
  *
  * The operation.  For every batch item b, head h and query row i:
  *
@@ -218,6 +218,48 @@ fa_status fa_decode_paged_bf16(const fa_bf16 *q, const fa_bf16 *k_cache, const f
                                fa_bf16 *o, float *lse,
                                int B, int H, int d, int page_size, int max_pages, int num_pages,
                                float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * FP8 forward, step 1: rotate and encode one of Q or K.  Every row x (length d)
+ * of the bf16 tensor becomes y = H (signs * x), with H the unnormalised
+ * Sylvester-Hadamard matrix (entries +-1, so H H^T = d I) applied as the
+ * butterfly in fp32 (stages h = 1, 2, ..., d/2; (a, b) -> (a + b, a - b)); per
+ * tile of tile_rows consecutive rows of one head, e = the smallest integer with
+ * max |y| <= 448 * 2^e (clamped to [-127, 127]; 0 for an all-zero tile) and the
+ * codes are E4M3(y * 2^-e), OCP FP8 with 4 exponent bits (bias 7) and 3 mantissa
+ * bits, rounded to nearest even.  This is FlashAttention-3's FP8 recipe: one
+ * scale per tile and incoherent processing by random signs plus a Hadamard
+ * transform ("FlashAttention 1–4 ...", section "FlashAttention-3"); the scales
+ * are powers of two so that encoding is exact up to the E4M3 rounding.
+ *
+ * x [B, H, N, d] bf16, 16-byte aligned; signs [d] int8, each +1 or -1 (the
+ * same vector for Q and K); codes [B, H, N, d] uint8 output, 16-byte aligned;
+ * exps [B, H, ceil(N / tile_rows)] int32 output, 4-byte aligned.  tile_rows is
+ * 32 for Q and 64 for K (the tiles fa_fwd_fp8 reads); d in {64, 128}.  Inputs
+ * must be finite with d * max |x| below the fp32 range.  Outputs must not
+ * overlap the inputs or each other.  Errors as for the forward.
+ */
+fa_status fa_fp8_quantize_bf16(const fa_bf16 *x, const int8_t *signs, uint8_t *codes, int32_t *exps,
+                               int B, int H, int N, int d, int tile_rows, void *stream);
+
+/*
+ * FP8 forward, step 2: attention with Q and K given as E4M3 codes from
+ * fa_fp8_quantize_bf16 (q with tile_rows 32, k with tile_rows 64, both with the
+ * same signs) and V in bf16:
+ *
+ *   s_ij = (scale / d) * sum_c deq(q_i)_c deq(k_j)_c,   deq = E4M3 value * 2^e of the row's tile,
+ *
+ * then o and lse exactly as fa_fwd_bf16 (masks, layouts, empty rows).  Since
+ * (H s q).(H s k) = d q.k, this is attention of the original q and k up to the
+ * E4M3 rounding of the rotated rows.  The products run on gfx950's FP8 matrix
+ * instructions with the tiles' exponents as block scales; P is rounded to bf16
+ * for P V as in the bf16 kernel.  q_codes, k_codes, v, o 16-byte aligned;
+ * q_exps, k_exps, lse, kv_limit 4-byte aligned; o and lse must not overlap an
+ * input or each other.  Errors as for the forward.
+ */
+fa_status fa_fwd_fp8(const uint8_t *q_codes, const int32_t *q_exps, const uint8_t *k_codes, const int32_t *k_exps,
+                     const fa_bf16 *v, fa_bf16 *o, float *lse, int B, int H, int N, int d, int causal, float scale,
+                     const int32_t *kv_limit, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status s);

@@ -191,3 +191,36 @@ def test_decode_workspace_bytes(lib):
     assert f(2, 32, 128, 128) == (2 * 32 * 8 * 128 + 2 * 32 * 8 * 2) * 4
     assert f(1, 1, 64, 1) == (64 + 64) * 4
     assert f(0, 1, 128, 1) == 0 and f(1, 1, 96, 1) == 0 and f(1, 1, 128, 0) == 0
+
+
+# FP8: fake addresses past the ones above
+XQ, SG, CQ, EQ, CK, EK, VF, OF, LF = (0x10000000 * (i + 40) for i in range(9))
+
+
+def quant(lib, x=XQ, sg=SG, c=CQ, e=EQ, B=2, H=3, N=100, d=128, tile=32):
+    return lib.fa_fp8_quantize_bf16(x, sg, c, e, B, H, N, d, tile, None)
+
+
+def fwd8(lib, qc=CQ, qe=EQ, kc=CK, ke=EK, v=VF, o=OF, l=LF, B=2, H=3, N=100, d=128, causal=0, scale=0.125, m=None):
+    return lib.fa_fwd_fp8(qc, qe, kc, ke, v, o, l, B, H, N, d, causal, scale, m, None)
+
+
+def test_fp8_validation(lib):
+    assert quant(lib, sg=None) == 1
+    assert quant(lib, e=None) == 1
+    assert quant(lib, N=0) == 2
+    assert quant(lib, tile=16) == 2          # tiles of 32 (q) or 64 (k) rows only
+    assert quant(lib, d=96) == 3
+    assert quant(lib, x=XQ + 2) == 5
+    assert quant(lib, c=CQ + 8) == 5
+    assert quant(lib, e=EQ + 2) == 5
+    assert quant(lib, c=XQ + 64) == 8         # codes over the input
+    assert quant(lib, e=CQ + 4) == 8          # exponents over the codes
+    assert fwd8(lib, qe=None) == 1
+    assert fwd8(lib, N=0) == 2
+    assert fwd8(lib, d=32) == 3
+    assert fwd8(lib, scale=-1.0) == 4
+    assert fwd8(lib, kc=CK + 4) == 5
+    assert fwd8(lib, ke=EK + 1) == 5
+    assert fwd8(lib, o=VF) == 8               # output over an input
+    assert fwd8(lib, l=OF + 64) == 8          # lse over the output
