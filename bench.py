@@ -28,7 +28,13 @@ Besides the headline number the line carries:
                   o, lse, block-table entries) per call / mean call time, against
                   8000 GB/s; its oracle baseline runs the whole workload.
 
---path backward / --path decode make that pass the timed step instead.
+  fp8          -- the FP8 forward on the same workload: the attention kernel
+                  alone (E4M3 Q and K codes already in device memory) and the
+                  whole path with the quantisation of Q and K; roofline against
+                  the mixed peak of FP8 Q K^T (5000) and bf16 P V (2500),
+                  1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TFLOP/s.
+
+--path backward / --path decode / --path fp8 make that pass the timed step instead.
 """
 from __future__ import annotations
 
@@ -47,6 +53,8 @@ BWD_METRIC = "attention bwd TFLOP/s (bf16, nominal 10*N^2*d per head) and % of M
 DEC_METRIC = "paged decode attention GB/s (bf16, keys and values read once) and % of MI355X HBM bandwidth"
 PEAK_HBM_GBS = 8000.0
 DECODE_HEADLINE = "decode_b64h32d128_len2048"
+FP8_METRIC = "attention fwd TFLOP/s with FP8 (E4M3) Q and K, bf16 V, and % of the mixed FP8/bf16 MFMA peak"
+PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 
 # Sources each timed path is built from: a traffic figure measured on other
 # sources is stale and is not reported.
@@ -57,6 +65,7 @@ KERNEL_SOURCES = {
     "unfused": ["fa_unfused.hip", "fa_common.h"],
     "backward": ["fa_bwd_bf16.hip", "fa_tile.h", "fa_common.h"],
     "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_launch.h"],
+    "fp8": ["fa_fwd_fp8.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
 }
 
 
@@ -206,6 +215,74 @@ def decode_entry(torch, binding, xd, steps, warmup, traffic_file, cpu: bool):
     return entry
 
 
+def measure_fp8(torch, binding, x, steps, warmup):
+    """(ms of the FP8 attention kernel alone, ms of quantise Q + quantise K + attention)."""
+    from flashattention_forward_attn_amd import inputs
+    w = x.workload
+    q, k, v, lim = device_inputs(torch, x)
+    signs = torch.from_numpy(inputs.fp8_signs(w.d)).cuda()
+    qc, qe = binding.fp8_quantize(q, signs, binding.FP8_Q_TILE)
+    kc, ke = binding.fp8_quantize(k, signs, binding.FP8_K_TILE)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def attend():
+        binding.fa_fwd_fp8(qc, qe, kc, ke, v, o, lse, w.causal, w.scale, lim, stream)
+
+    def whole():
+        binding.fa_fp8_quantize_bf16(q, signs, qc, qe, binding.FP8_Q_TILE, stream)
+        binding.fa_fp8_quantize_bf16(k, signs, kc, ke, binding.FP8_K_TILE, stream)
+        attend()
+
+    ms = time_launches(torch, attend, steps, warmup)
+    ms_whole = time_launches(torch, whole, max(10, steps // 2), max(5, warmup // 4))
+    del q, k, v, lim, signs, qc, qe, kc, ke, o, lse
+    return ms, ms_whole
+
+
+def cpu_baseline_fp8(x, target_seconds: float):
+    """The oracle's FP8 path (quantise, then attention on the codes) on the first heads."""
+    import oracle
+    from flashattention_forward_attn_amd import inputs
+    w = x.workload
+    threads = host_threads()
+    signs = inputs.fp8_signs(w.d)
+    nh = 1
+    while True:
+        sl = lambda a: np.ascontiguousarray(a[:1, :nh], dtype=np.float64)
+        q, k, v = sl(x.q), sl(x.k), sl(x.v)
+        lim = None if x.kv_limit is None else np.ascontiguousarray(x.kv_limit[:1])
+        t0 = time.perf_counter()
+        qc, qe = oracle.fp8_quantize(q, signs, tile_rows=32, nthreads=threads)
+        kc, ke = oracle.fp8_quantize(k, signs, tile_rows=64, nthreads=threads)
+        oracle.attention_fp8(qc, qe, 32, kc, ke, 64, v, causal=w.causal, scale=w.scale, kv_limit=lim, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt * 2 > target_seconds or nh * 2 > w.H:
+            break
+        nh *= 2
+    flops = w.flops() / (w.B * w.H) * nh
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"heads 0..{nh - 1} of batch item 0 of {w.name}: quantisation and attention on the codes, "
+                      f"fp64, {dt:.1f} s", "seconds": round(dt, 3)}
+
+
+def fp8_entry(torch, binding, x, steps, warmup, traffic_file, cpu: bool, cpu_seconds: float):
+    w = x.workload
+    ms, ms_whole = measure_fp8(torch, binding, x, steps, warmup)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    entry = {"metric": FP8_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+             "with_quantisation": {"ms_per_step": round(ms_whole, 5),
+                                   "TFLOP/s": round(w.flops() / (ms_whole * 1e-3) / 1e12, 2)},
+             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_FP8_MIXED_TFLOPS, 1),
+                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_MIXED_TFLOPS, 4),
+                          "traffic": load_traffic(traffic_file, "fp8", w.name),
+                          "note": "attention kernel alone; half the nominal FLOPs on FP8 (Q K^T), half on bf16 (P V)"}}
+    if cpu:
+        entry["cpu_baseline"] = cpu_baseline_fp8(x, cpu_seconds)
+    return entry
+
+
 def effective_flops(x) -> float:
     """FLOPs of the valid (query, key) pairs only: 4 d per pair."""
     w = x.workload
@@ -294,9 +371,9 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
-    ap.add_argument("--path", choices=("fused", "unfused", "backward", "decode"), default="fused",
+    ap.add_argument("--path", choices=("fused", "unfused", "backward", "decode", "fp8"), default="fused",
                     help="time the fused kernel (default), the unfused three-kernel baseline, the "
-                         "backward pass or the paged decode as the step")
+                         "backward pass, the paged decode or the FP8 forward as the step")
     ap.add_argument("--decode-workload", default=DECODE_HEADLINE)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
@@ -337,6 +414,23 @@ def main() -> int:
                            "max_len": xd.workload.max_len, "page": 16, "path": "decode",
                            "bytes_per_step": entry["bytes_per_step"], "parallelism": "single GPU"},
                 "roofline": entry["roofline"]}
+        if "cpu_baseline" in entry:
+            line["cpu_baseline"] = entry["cpu_baseline"]
+        print(json.dumps(line), flush=True)
+        return 0
+
+    if args.path == "fp8":
+        w = inputs.WORKLOADS[args.workload]
+        x = inputs.generate(w)
+        entry = fp8_entry(torch, binding, x, args.steps, args.warmup, args.traffic, not args.no_cpu_baseline,
+                          args.cpu_seconds)
+        line = {"metric": FP8_METRIC, "value": entry["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": entry["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 (Q, K) / bf16 (V, P)",
+                "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
+                "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                           "path": "fp8", "flops_per_step": w.flops(), "parallelism": "single GPU"},
+                "roofline": entry["roofline"], "with_quantisation": entry["with_quantisation"]}
         if "cpu_baseline" in entry:
             line["cpu_baseline"] = entry["cpu_baseline"]
         print(json.dumps(line), flush=True)
@@ -411,6 +505,8 @@ def main() -> int:
         }
         if not args.no_cpu_baseline:
             line["backward"]["cpu_baseline"] = cpu_baseline_backward(x, g)
+        line["fp8"] = fp8_entry(torch, binding, x, args.steps, args.warmup, args.traffic, not args.no_cpu_baseline,
+                                args.cpu_seconds)
         xd = inputs.generate_decode(inputs.DECODE_WORKLOADS[args.decode_workload])
         line["decode"] = decode_entry(torch, binding, xd, max(20, args.steps // 2), max(10, args.warmup // 4),
                                       args.traffic, not args.no_cpu_baseline)
