@@ -58,14 +58,14 @@ PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 
 # Sources each timed path is built from: a traffic figure measured on other
 # sources is stale and is not reported.
-# (fa_launch.h holds host-side declarations only, except the decode path's page
-# and split sizes.)
+# (fa_launch.h holds host-side declarations only; the sizes kernels share with
+# the host live in fa_sizes.h.)
 KERNEL_SOURCES = {
     "fused": ["fa_fwd_bf16.hip", "fa_tile.h", "fa_common.h"],
     "unfused": ["fa_unfused.hip", "fa_common.h"],
     "backward": ["fa_bwd_bf16.hip", "fa_tile.h", "fa_common.h"],
-    "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_launch.h"],
-    "fp8": ["fa_fwd_fp8.hip", "fa_tile.h", "fa_common.h", "fa_launch.h"],
+    "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_sizes.h"],
+    "fp8": ["fa_fwd_fp8.hip", "fa_tile.h", "fa_common.h", "fa_sizes.h"],
 }
 
 
@@ -75,6 +75,17 @@ def host_threads() -> int:
     except AttributeError:
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def device_inputs(torch, x):
@@ -194,7 +205,7 @@ def cpu_baseline_decode(xd):
     t0 = time.perf_counter()
     oracle.decode_paged(q, kc, vc, xd.block_table, xd.seq_lens, xd.workload.scale, nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": f"the whole {xd.workload.name} workload, fp64, {dt:.3f} s; same algorithmic bytes",
             "seconds": round(dt, 3)}
 
@@ -262,7 +273,7 @@ def cpu_baseline_fp8(x, target_seconds: float):
             break
         nh *= 2
     flops = w.flops() / (w.B * w.H) * nh
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": f"heads 0..{nh - 1} of batch item 0 of {w.name}: quantisation and attention on the codes, "
                       f"fp64, {dt:.1f} s", "seconds": round(dt, 3)}
 
@@ -316,7 +327,7 @@ def cpu_baseline(x, target_seconds: float):
         "value": ids.size * flops_per_row / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": host_cpu_model(),
         "sample": f"{ids.size} of {rows_total} query rows of {w.name}, evenly spaced, fp64, "
                   f"{dt:.1f} s; FLOPs per row = workload FLOPs / rows",
         "seconds": round(dt, 3),
@@ -341,7 +352,7 @@ def cpu_baseline_backward(x, g):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": nh,
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": host_cpu_model(),
         "sample": f"full backward of heads 0..{nh - 1} of batch item 0 of {w.name}, fp64, {dt:.1f} s; "
                   f"nominal backward FLOPs of those heads",
         "seconds": round(dt, 3),

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_sizes.h"
+
 namespace fa {
 
 hipError_t launch_fused_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -34,31 +36,10 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, bool causal,
                            float scale, const int32_t* kv_limit, float* workspace, hipStream_t stream);
 
-// Decode over a paged cache: pages of kDecodePage tokens; the key range of a
-// sequence is split into pieces of kDecodeSplitKeys keys (one workgroup each).
-// The workspace holds the splits' unnormalised outputs (fp32 [B*H*max_splits, d], padded to 64
-// floats) and then their (max, sum) pairs (fp32 [B*H*max_splits, 2]).
-constexpr int kDecodePage = 16;
-constexpr int kDecodeSplitKeys = 256;
-inline int64_t decode_max_splits(int max_pages) {
-    return ((int64_t)max_pages * kDecodePage + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
-}
-inline int64_t decode_part_o_floats(int B, int H, int d, int max_pages) {
-    return ((int64_t)B * H * decode_max_splits(max_pages) * d + 63) / 64 * 64;
-}
-inline int64_t decode_workspace_floats(int B, int H, int d, int max_pages) {
-    return decode_part_o_floats(B, H, d, max_pages) + ((int64_t)B * H * decode_max_splits(max_pages) * 2 + 63) / 64 * 64;
-}
-
 // Two launches: per-split partials, then the merge into o and lse.
 hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, void* o, float* lse, int B, int H, int d, int max_pages,
                               int num_pages, float scale, float* workspace, hipStream_t stream);
-
-// FP8 forward: Q codes come in tiles of kFp8QTile rows, K codes in tiles of
-// kFp8KTile rows, one int32 exponent per tile ([B, H, ceil(N / tile)]).
-constexpr int kFp8QTile = 32;
-constexpr int kFp8KTile = 64;
 
 // Rotate (random signs, Hadamard) and encode rows of a bf16 [B, H, N, d] tensor
 // to E4M3 codes [B, H, N, d] with per-tile exponents.
