@@ -49,17 +49,29 @@ __device__ __forceinline__ i32x4 dma_desc(const void* base, uint32_t bytes) {
 }
 
 // Wave-wide load straight into LDS: lane l's 16 bytes at global offset voff land at
-// LDS byte address dst + 16 l (M0 holds dst).  Issued from inline assembly so that
+// LDS byte address dst + 16 l (M0 holds dst while the load issues; the load takes
+// its LDS address at issue, and M0's previous value is restored afterwards, so
+// the compiler's view of M0 is unchanged).  Issued from inline assembly so that
 // the compiler does not wait for it before unrelated LDS reads; the caller waits
 // with s_waitcnt vmcnt before the barrier that publishes the data.
 __device__ __forceinline__ void dma16(const i32x4& desc, uint32_t dst, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc) : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc)
+        : "memory");
 }
 // The same with 4 bytes per lane (lane l's word lands at dst + 4 l).
 __device__ __forceinline__ void dma4(const i32x4& desc, uint32_t dst, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc) : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(desc)
+        : "memory");
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives, in
