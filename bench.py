@@ -115,7 +115,24 @@ def time_launches(torch, launch, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
-def measure_fused(torch, binding, x, steps, warmup):
+def launch_spread(torch, launch, n: int) -> dict:
+    """Median and minimum milliseconds of n single launches, each between its own
+    pair of HIP events on the launch stream (run after, and apart from, the timed
+    steps, whose mean is the reported rate)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"launches": n, "median_ms": round(t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2]), 5),
+            "min_ms": round(t[0], 5)}
+
+
+def measure_fused(torch, binding, x, steps, warmup, spread=0):
+    """Mean ms per fused launch; with spread > 0 also launch_spread over that many launches."""
     w = x.workload
     q, k, v, lim = device_inputs(torch, x)
     o = torch.empty_like(q)
@@ -127,8 +144,9 @@ def measure_fused(torch, binding, x, steps, warmup):
         fn(q, k, v, o, lse, w.causal, w.scale, lim, stream)
 
     ms = time_launches(torch, launch, steps, warmup)
+    sp = launch_spread(torch, launch, spread) if spread else None
     del q, k, v, o, lse, lim
-    return ms
+    return (ms, sp) if spread else ms
 
 
 def measure_unfused(torch, binding, x, steps, warmup):
@@ -147,8 +165,9 @@ def measure_unfused(torch, binding, x, steps, warmup):
     return ms
 
 
-def measure_backward(torch, binding, x, g, steps, warmup):
-    """Mean ms per fa_bwd_bf16 call (three launches) on O and LSE from one forward."""
+def measure_backward(torch, binding, x, g, steps, warmup, spread=0):
+    """Mean ms per fa_bwd_bf16 call (three launches) on O and LSE from one forward;
+    with spread > 0 also launch_spread over that many calls."""
     w = x.workload
     q, k, v, lim = device_inputs(torch, x)
     o, lse = binding.attention(q, k, v, causal=w.causal, scale=w.scale, kv_limit=lim)
@@ -161,8 +180,9 @@ def measure_backward(torch, binding, x, g, steps, warmup):
         binding.fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, w.causal, w.scale, lim, ws, stream)
 
     ms = time_launches(torch, launch, steps, warmup)
+    sp = launch_spread(torch, launch, spread) if spread else None
     del q, k, v, o, lse, lim, dout, dq, dk, dv, ws
-    return ms
+    return (ms, sp) if spread else ms
 
 
 def decode_bytes(xd) -> int:
@@ -453,12 +473,15 @@ def main() -> int:
         return 2
     x = inputs.generate(w)
     g = inputs.grad_output(w) if w.dtype == "bf16" else None
+    spread = None
     if args.path == "backward":
-        ms = measure_backward(torch, binding, x, g, args.steps, args.warmup)
+        ms, spread = measure_backward(torch, binding, x, g, args.steps, args.warmup, spread=SPREAD_LAUNCHES)
         tflops = w.bwd_flops() / (ms * 1e-3) / 1e12
+    elif args.path == "fused":
+        ms, spread = measure_fused(torch, binding, x, args.steps, args.warmup, spread=SPREAD_LAUNCHES)
+        tflops = w.flops() / (ms * 1e-3) / 1e12
     else:
-        measure = measure_fused if args.path == "fused" else measure_unfused
-        ms = measure(torch, binding, x, args.steps, args.warmup)
+        ms = measure_unfused(torch, binding, x, args.steps, args.warmup)
         tflops = w.flops() / (ms * 1e-3) / 1e12
     traffic = load_traffic(args.traffic, args.path, w.name)
 
@@ -482,6 +505,11 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if spread is not None:
+        fl = w.bwd_flops() if args.path == "backward" else w.flops()
+        spread["TFLOP/s_at_median"] = round(fl / (spread["median_ms"] * 1e-3) / 1e12, 2)
+        spread["TFLOP/s_at_min"] = round(fl / (spread["min_ms"] * 1e-3) / 1e12, 2)
+        line["per_launch"] = spread
     if args.path == "unfused":
         line["roofline"]["bound"] = "hbm"
         line["roofline"]["note"] = "three kernels per step; see unfused bytes in the profile summary"
@@ -530,6 +558,9 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     return 0
 
+
+# single launches timed one by one after the timed steps (median and minimum)
+SPREAD_LAUNCHES = 51
 
 BWD_NOTE = ("one call = three launches (row statistics, dK/dV, dQ); achieved = nominal FLOPs "
             "(10*N^2*d per head, halved for causal) / mean call time; the kernels execute 14*N^2*d "

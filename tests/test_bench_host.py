@@ -1,0 +1,42 @@
+"""Host-side logic of bench.py (no GPU): the single-GPU guard, and the rule that a
+stored traffic figure is reported only while the kernel sources it was measured
+on are unchanged."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("path", sorted(bench.KERNEL_SOURCES))
+def test_kernel_sources_exist(path):
+    here = os.path.join(ROOT, "flashattention_forward_attn_amd", "csrc")
+    for name in bench.KERNEL_SOURCES[path]:
+        assert os.path.isfile(os.path.join(here, name)), name
+    assert len(bench._kernel_digest(path)) == 64
+
+
+def test_traffic_reported_only_for_current_sources(tmp_path):
+    f = tmp_path / "traffic.json"
+    good = {"bytes_per_launch": 123, "kernel_source_sha256": bench._kernel_digest("fused")}
+    stale = {"bytes_per_launch": 456, "kernel_source_sha256": "0" * 64}
+    f.write_text(json.dumps({"fused": {"w_good": good, "w_stale": stale}}))
+    assert bench.load_traffic(str(f), "fused", "w_good") == 123
+    assert bench.load_traffic(str(f), "fused", "w_stale") is None
+    assert bench.load_traffic(str(f), "fused", "w_missing") is None
+    assert bench.load_traffic(str(f), "decode", "w_good") is None
+    assert bench.load_traffic(str(tmp_path / "absent.json"), "fused", "w_good") is None
+
