@@ -30,14 +30,30 @@ constexpr int kUnfusedMaxN = 32768;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Size limits of the [B, H, N, d] paths.  Tensors are addressed with 64-bit
+// offsets; two quantities stay 32-bit.  A buffer descriptor spans one head, so
+// N * d * elem must fit in 32 bits.  A grid dimension holds at most 2^32 - 1
+// work-items, and no launch uses more than 512 threads per 32 rows of a head
+// (the row-statistics kernel runs 16 threads per row; the others fewer), so
+// B * H * ceil(N / 32) * 512 must fit in 32 bits: at most 2^23 - 1 row tiles,
+// e.g. B * H * N < 2^28 when N is a multiple of 32.
+constexpr int64_t kMaxThreadsPerTile = 512;
+
+bool shape_ok(int B, int H, int N, int d, int elem) {
+    if (B < 1 || H < 1 || N < 1) return false;
+    const int64_t tiles = (int64_t)B * H * ((N + 31) / 32);
+    if (tiles * kMaxThreadsPerTile > (int64_t)UINT32_MAX) return false;
+    return (int64_t)N * d * elem <= (int64_t)UINT32_MAX;
+}
+
 // Common checks for every entry point.  elem = bytes per q/k/v/o element.
 fa_status validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
                    int N, int d, float scale, const int32_t* kv_limit, int elem) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!shape_ok(B, H, N, d, elem)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (elems > INT32_MAX) return FA_ERR_SHAPE;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
         (kv_limit && !aligned(kv_limit, 4)))
@@ -146,8 +162,8 @@ fa_status fa_bwd_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (elems > INT32_MAX) return FA_ERR_SHAPE;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o, (const void*)dout,
                           (const void*)dq, (const void*)dk, (const void*)dv})
@@ -180,7 +196,8 @@ fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const f
                                void* workspace, size_t workspace_bytes_given, void* stream) {
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage ||
-        fa::decode_max_splits(max_pages) > 65535)
+        fa::decode_max_splits(max_pages) > 65535 ||
+        (int64_t)B * H * 256 > (int64_t)UINT32_MAX)  // 256 threads per (sequence, head) in each launch
         return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -210,8 +227,8 @@ fa_status fa_fp8_quantize_bf16(const fa_bf16* x, const int8_t* signs, uint8_t* c
     if (!x || !signs || !codes || !exps) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || (tile_rows != fa::kFp8QTile && tile_rows != fa::kFp8KTile)) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (elems > INT32_MAX) return FA_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(exps, 4)) return FA_ERR_ALIGN;
     const int64_t ntile = (int64_t)B * H * ((N + tile_rows - 1) / tile_rows);
     const Range ins[] = {span(x, elems * 2), span(signs, d)};
@@ -230,8 +247,8 @@ fa_status fa_fwd_fp8(const uint8_t* q_codes, const int32_t* q_exps, const uint8_
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (elems > INT32_MAX) return FA_ERR_SHAPE;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(q_exps, 4) ||
         !aligned(k_exps, 4) || !aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4)))

@@ -306,3 +306,50 @@ def outlier_qkv(B: int, H: int, N: int, d: int, seed: int = 0, n_out: int = 4, m
     q *= 0.25
     k *= 0.25
     return tuple(bf16_to_f32(bf16_bits(a)) for a in (q, k, v))
+
+
+# ---------------------------------------------------------------- tensors beyond 2^31 elements
+#
+# A [B, H, N, d] shape whose tensors hold more than 2^31 elements, mostly zero:
+# only the listed (batch, head) pairs carry data, drawn from
+# ``default_rng([seed, 5])`` in the order Q, K, V, dO (float32 standard normal,
+# rounded to bf16), each of shape [len(heads), N, d].  Every row sees the first
+# `limit` keys (kv_limit = limit for all rows).  The last two listed pairs start
+# past element 2^31, so a 32-bit element offset would miss them.
+
+@dataclasses.dataclass(frozen=True)
+class LargeCase:
+    B: int = 2
+    H: int = 8256
+    N: int = 1024
+    d: int = 128
+    limit: int = 64
+    heads: tuple = (0, 8000, 16384, 16511)   # flattened b * H + h
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def elements(self) -> int:
+        return self.B * self.H * self.N * self.d
+
+
+@dataclasses.dataclass
+class LargeInputs:
+    case: LargeCase
+    q_bits: np.ndarray     # uint16 [S, N, d] for the listed heads
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    dout_bits: np.ndarray
+
+    def values(self, name: str) -> np.ndarray:
+        """float64 values of one of q, k, v, dout as [1, S, N, d]."""
+        return bf16_to_f32(getattr(self, name + "_bits")).astype(np.float64)[None]
+
+
+def generate_large(case: LargeCase = LargeCase()) -> LargeInputs:
+    rng = np.random.default_rng([case.seed, 5])
+    shape = (len(case.heads), case.N, case.d)
+    bits = [bf16_bits(rng.standard_normal(shape).astype(np.float32)) for _ in range(4)]
+    return LargeInputs(case, *bits)

@@ -30,8 +30,11 @@
  * clamped to [0, N] (negative counts as 0).  Causal masking is top-left aligned
  * with the diagonal included (query i sees keys 0..i).
  *
- * Supported shapes.  d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^31 elements per
- * tensor (the unfused path also needs B*H <= 65535 and N <= 32768).  scale must be finite and
+ * Supported shapes.  d in {64, 128}; B, H, N >= 1; one head of one tensor below
+ * 4 GiB (N*d*2 bytes in bf16, N*d*4 in fp32); and B*H*ceil(N/32) < 2^23 row tiles
+ * of 32, i.e. B*H*N < 2^28 rows when N is a multiple of 32 (68 GB per bf16
+ * tensor at d = 128).  Offsets are 64-bit, so a tensor may exceed 2^31 elements.
+ * The unfused path also needs B*H <= 65535 and N <= 32768.  scale must be finite and
  * positive (the pages use 1/sqrt(d)).
  *
  * Memory and ownership.  Every pointer is device memory owned by the caller.  The
@@ -62,7 +65,7 @@ typedef uint16_t fa_bf16; /* raw bf16 bits (the upper half of an IEEE fp32) */
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL                              */
-    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 - 1 elements    */
+    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or sizes beyond the supported shapes     */
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                      */
     FA_ERR_SCALE = 4,     /* scale is NaN, infinite, zero or negative                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
@@ -196,8 +199,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int max_pages);
  * Layout.  q, o: contiguous [B, H, d] bf16.  k_cache, v_cache: contiguous
  * [num_pages, H, 16, d] bf16 (one page of one head is 16 * d contiguous values).
  * block_table: contiguous [B, max_pages] int32.  seq_lens: [B] int32.  lse:
- * [B, H] fp32.  page_size must be 16; d in {64, 128}; B, H in [1, 65535];
- * max_pages in [1, 1048560] (at most 65535 splits of 256 keys); num_pages >= 1.
+ * [B, H] fp32.  page_size must be 16; d in {64, 128}; B, H in [1, 65535] with
+ * B*H < 2^24; max_pages in [1, 1048560] (at most 65535 splits of 256 keys);
+ * num_pages >= 1.
  *
  * Contents.  Lengths are clamped to [0, max_pages * 16].  Block-table entries of
  * pages past a sequence's length are never read; an entry inside the length that

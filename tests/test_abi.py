@@ -224,3 +224,36 @@ def test_fp8_validation(lib):
     assert fwd8(lib, ke=EK + 1) == 5
     assert fwd8(lib, o=VF) == 8               # output over an input
     assert fwd8(lib, l=OF + 64) == 8          # lse over the output
+
+
+def test_size_limits(lib):
+    """Tensors above 2^31 elements pass the shape check (offsets are 64-bit); the
+    limits are one head below 4 GiB and fewer than 2^23 tiles of 32 rows.  An
+    accepted size returns the next check's error (scale, then alignment), so
+    nothing is launched."""
+    nan = float("nan")
+    big = dict(B=1, H=3, N=1 << 23, d=128)                      # 3 * 2^30 elements per tensor
+    assert fwd(lib, scale=nan, **big) == 4
+    assert fwd(lib, "fa_fwd_f32", scale=nan, B=1, H=5, N=1 << 22, d=128) == 4   # 5 * 2^29
+    assert bwd(lib, scale=nan, **big) == 4
+    assert fwd8(lib, scale=nan, **big) == 4
+    assert quant(lib, x=XQ + 2, **big) == 5
+    # one head: N * d * bytes must stay below 2^32
+    assert fwd(lib, scale=nan, B=1, H=1, N=(1 << 24) - 1, d=128) == 4
+    assert fwd(lib, scale=nan, B=1, H=1, N=1 << 24, d=128) == 2
+    assert fwd(lib, "fa_fwd_f32", scale=nan, B=1, H=1, N=(1 << 23) - 1, d=128) == 4
+    assert fwd(lib, "fa_fwd_f32", scale=nan, B=1, H=1, N=1 << 23, d=128) == 2
+    assert bwd(lib, scale=nan, B=1, H=1, N=1 << 24, d=128) == 2
+    assert fwd8(lib, scale=nan, B=1, H=1, N=1 << 24, d=128) == 2
+    assert quant(lib, x=XQ + 2, B=1, H=1, N=1 << 24, d=128) == 2
+    # grid: B * H * ceil(N / 32) < 2^23 tiles of 32 rows
+    assert fwd(lib, scale=nan, B=1, H=(1 << 23) - 1, N=1, d=64) == 4
+    assert fwd(lib, scale=nan, B=1, H=1 << 23, N=1, d=64) == 2
+    assert fwd(lib, scale=nan, B=2, H=(1 << 21) - 1, N=33, d=64) == 4
+    assert fwd(lib, scale=nan, B=2, H=1 << 21, N=33, d=64) == 2
+    assert bwd(lib, scale=nan, B=1 << 12, H=1 << 11, N=32, d=64) == 2
+    assert fwd8(lib, scale=nan, B=1 << 12, H=1 << 11, N=32, d=64) == 2
+    assert quant(lib, x=XQ + 2, B=1 << 12, H=1 << 11, N=32, d=64) == 2
+    # decode: 256 threads per (sequence, head) in one grid dimension
+    assert dec(lib, scale=0.0, B=65535, H=256) == 4
+    assert dec(lib, scale=0.0, B=65535, H=257) == 2
