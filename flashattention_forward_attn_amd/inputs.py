@@ -353,3 +353,57 @@ def generate_large(case: LargeCase = LargeCase()) -> LargeInputs:
     shape = (len(case.heads), case.N, case.d)
     bits = [bf16_bits(rng.standard_normal(shape).astype(np.float32)) for _ in range(4)]
     return LargeInputs(case, *bits)
+
+
+# A paged cache whose pool holds more than 2^31 elements per cache, mostly zero:
+# the sequences' pages are the last pages of the pool (past element 2^31), in a
+# shuffled order.  Draw order from ``default_rng([seed, 6])``: the order of the
+# used pages, q (B, H, d), then the used pages of k and v (float32 standard
+# normal, rounded to bf16).  Block-table entries past a sequence's pages are 0.
+
+@dataclasses.dataclass(frozen=True)
+class LargeDecodeCase:
+    H: int = 32
+    d: int = 128
+    num_pages: int = 33000
+    seq_lens: tuple = (37, 300)
+    seed: int = 0
+
+    @property
+    def B(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def max_pages(self) -> int:
+        return max(-(-n // DECODE_PAGE) for n in self.seq_lens)
+
+    def page_elements(self) -> int:
+        return self.H * DECODE_PAGE * self.d
+
+
+@dataclasses.dataclass
+class LargeDecodeInputs:
+    case: LargeDecodeCase
+    q_bits: np.ndarray        # uint16 (B, H, d)
+    pages: np.ndarray         # int32: pool index of each used page, in table order
+    k_bits: np.ndarray        # uint16 (len(pages), H, 16, d), the used pages only
+    v_bits: np.ndarray
+    block_table: np.ndarray   # int32 (B, max_pages), pool indices
+    seq_lens: np.ndarray      # int32 (B,)
+
+
+def generate_large_decode(case: LargeDecodeCase = LargeDecodeCase()) -> LargeDecodeInputs:
+    rng = np.random.default_rng([case.seed, 6])
+    counts = [-(-n // DECODE_PAGE) for n in case.seq_lens]
+    used = sum(counts)
+    pages = (case.num_pages - used + rng.permutation(used)).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((case.B, case.H, case.d)).astype(np.float32))
+    shape = (used, case.H, DECODE_PAGE, case.d)
+    k = bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    v = bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    table = np.zeros((case.B, case.max_pages), np.int32)
+    at = 0
+    for b, n in enumerate(counts):
+        table[b, :n] = pages[at:at + n]
+        at += n
+    return LargeDecodeInputs(case, q, pages, k, v, table, np.asarray(case.seq_lens, np.int32))

@@ -159,3 +159,29 @@ def test_fp8(data):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
     assert np.abs(gl - rl).max() <= LSE_ABS
     check_zero_heads(torch, o, lse)
+
+
+def test_decode_pool_past_2_31():
+    """Paged decode whose sequences live in the last pages of a 4.3 GB pool (past
+    element 2^31 of each cache), against the oracle on a pool of just those pages."""
+    torch = cuda()
+    c = inputs.LargeDecodeCase()
+    x = inputs.generate_large_decode(c)
+    assert int(x.pages.min()) * c.page_elements() >= 2 ** 31
+    dev16 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    caches = []
+    for bits in (x.k_bits, x.v_bits):
+        t = torch.zeros((c.num_pages, c.H, inputs.DECODE_PAGE, c.d), dtype=torch.bfloat16, device="cuda")
+        t.index_copy_(0, torch.from_numpy(x.pages.astype(np.int64)).cuda(), dev16(bits))
+        caches.append(t)
+    o, lse = binding.decode_paged(dev16(x.q_bits), caches[0], caches[1], torch.from_numpy(x.block_table).cuda(),
+                                  torch.from_numpy(x.seq_lens).cuda())
+    torch.cuda.synchronize()
+    local = {int(p): i for i, p in enumerate(x.pages)}
+    table = np.vectorize(lambda p: local.get(int(p), 0))(x.block_table).astype(np.int32)
+    f64 = lambda bits: inputs.bf16_to_f32(bits).astype(np.float64)
+    ro, rl = oracle.decode_paged(f64(x.q_bits), f64(x.k_bits), f64(x.v_bits), table, x.seq_lens,
+                                 nthreads=oracle_threads())
+    err = np.abs(o.float().cpu().numpy() - ro)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+    assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_ABS
