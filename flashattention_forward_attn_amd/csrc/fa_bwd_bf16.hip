@@ -119,6 +119,34 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
     const int kw0 = k0 + pair * kKPW;        // first key of this wave pair
     const int kcol = kw0 + col;               // this lane's key
 
+    // A key block that no row can see (every row's key limit at or below its
+    // first key, as with key padding past a sequence's length) has zero
+    // gradients: store them without streaming any query tile.
+    if constexpr (MASK) {
+        __shared__ int row_limit_max[kWaves];
+        int m = 0;
+        for (int i = tid; i < N; i += kThreads)
+            m = max(m, row_key_limit(i, N, CAUSAL, kv_limit + (size_t)b * N + i));
+        m = wave_max_i(m);
+        if (lane == 0) row_limit_max[w] = m;
+        __syncthreads();
+        int seen = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) seen = max(seen, row_limit_max[i]);
+        if (seen <= k0) {
+            constexpr int kChunks = D / 8;  // 16-byte pieces of a row
+            for (int e = tid; e < kBKV * kChunks; e += kThreads) {
+                const int key = k0 + e / kChunks;
+                if (key < N) {
+                    const size_t off = head + (size_t)key * D + 8 * (e % kChunks);
+                    *reinterpret_cast<u32x4*>(dK + off) = u32x4{};
+                    *reinterpret_cast<u32x4*>(dV + off) = u32x4{};
+                }
+            }
+            return;
+        }
+    }
+
     // Direct loads: block g = i * kWaves + w of the stage's Q tile (g < kTileBlocks)
     // or dO tile; lane l's 16 bytes land at LDS position 16 l of the block.
     uint32_t dma_src[T::kPerWave], dma_dst[T::kPerWave];
