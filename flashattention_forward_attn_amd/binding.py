@@ -15,6 +15,9 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libfa.so")
+# the same entry points with the forward kernels built to use one LDS stage
+# (a race check for tests; never loaded by the product path)
+SINGLE_STAGE_LIBRARY = os.path.join(HERE, "libfa_single_stage.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
@@ -29,11 +32,17 @@ class FAError(RuntimeError):
         self.status = status
 
 
-def load(path: str = LIBRARY):
-    """Load libfa.so and declare the C signatures.  Raises if it is not built."""
+def load():
+    """Load libfa.so (once) and declare the C signatures.  Raises if it is not built."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = open_library(LIBRARY)
+    return _lib
+
+
+def open_library(path: str):
+    """A ctypes handle on a library exporting the C ABI of include/fa.h, with the
+    C signatures declared.  Raises if the file is missing."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m flashattention_forward_attn_amd.build`")
     lib = ctypes.CDLL(path)
@@ -61,7 +70,6 @@ def load(path: str = LIBRARY):
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

@@ -168,8 +168,8 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     __syncthreads();
 
     auto step = [&](auto stage_c, int t) {
-        constexpr int st = decltype(stage_c)::value;
-        if (t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
+        constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
+        if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
         const char* Sb = smem + st * T::kStage;
         const int kv0 = t * kBK;
 
@@ -240,6 +240,10 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                                                                         __builtin_bit_cast(bf16x8, pk[ks]),
                                                                         oacc[d32], 0, 0, 0);
                 }
+        }
+        if constexpr (kSingleStage) {
+            __syncthreads();  // every wave has finished reading the stage
+            if (t + 1 < ntiles) dma_tile(0, (t + 1) * kBK);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();

@@ -7,7 +7,17 @@
 
 #include "fa_common.h"
 
+// A build with FA_SINGLE_STAGE=1 streams K/V tiles through one LDS stage and
+// loads a tile only after every wave has finished reading the previous one, so
+// no load is in flight while a stage is read.  Its results must equal the
+// pipelined build's bit for bit: a check that the pipelining has no race.
+#ifndef FA_SINGLE_STAGE
+#define FA_SINGLE_STAGE 0
+#endif
+
 namespace fa {
+
+constexpr bool kSingleStage = FA_SINGLE_STAGE != 0;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef short i16x4 __attribute__((ext_vector_type(4)));

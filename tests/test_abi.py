@@ -38,6 +38,14 @@ def test_every_declared_function_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_single_stage_build_exports_the_same_functions():
+    """The race-check build of the forward kernels carries the whole ABI too."""
+    other = binding.open_library(binding.SINGLE_STAGE_LIBRARY)
+    for name in declared_functions():
+        assert hasattr(other, name), name
+    assert other.fa_fwd_bf16(None, K, V, O, L, 2, 3, 100, 128, 0, 0.125, None, None) == 1
+
+
 def test_status_strings(lib):
     for code in range(9):
         s = lib.fa_status_str(code).decode()
