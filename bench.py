@@ -197,7 +197,7 @@ def inputs_page(xd) -> int:
 
 
 def measure_decode(torch, binding, xd, steps, warmup):
-    """Mean ms per fa_decode_paged_bf16 call (split and combine launches)."""
+    """(mean ms per fa_decode_paged_bf16 call (split and combine launches), launch_spread of the calls)."""
     w = xd.workload
     dev16 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
     q, kc, vc = dev16(xd.q_bits), dev16(xd.k_bits), dev16(xd.v_bits)
@@ -213,8 +213,9 @@ def measure_decode(torch, binding, xd, steps, warmup):
         binding.fa_decode_paged_bf16(q, kc, vc, bt, sl, o, lse, w.scale, ws, stream)
 
     ms = time_launches(torch, launch, steps, warmup)
+    spread = launch_spread(torch, launch, SPREAD_LAUNCHES)
     del q, kc, vc, bt, sl, o, lse, ws
-    return ms
+    return ms, spread
 
 
 def cpu_baseline_decode(xd):
@@ -231,10 +232,12 @@ def cpu_baseline_decode(xd):
 
 
 def decode_entry(torch, binding, xd, steps, warmup, traffic_file, cpu: bool):
-    ms = measure_decode(torch, binding, xd, steps, warmup)
+    ms, spread = measure_decode(torch, binding, xd, steps, warmup)
     gbs = decode_bytes(xd) / (ms * 1e-3) / 1e9
+    spread["GB/s_at_median"] = round(decode_bytes(xd) / (spread["median_ms"] * 1e-3) / 1e9, 1)
+    spread["GB/s_at_min"] = round(decode_bytes(xd) / (spread["min_ms"] * 1e-3) / 1e9, 1)
     entry = {"metric": DEC_METRIC, "workload": xd.workload.name, "value": round(gbs, 1), "unit": "GB/s",
-             "ms_per_step": round(ms, 5), "bytes_per_step": decode_bytes(xd),
+             "ms_per_step": round(ms, 5), "per_launch": spread, "bytes_per_step": decode_bytes(xd),
              "TFLOP/s": round(xd.flops() / (ms * 1e-3) / 1e12, 2),
              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -247,7 +250,8 @@ def decode_entry(torch, binding, xd, steps, warmup, traffic_file, cpu: bool):
 
 
 def measure_fp8(torch, binding, x, steps, warmup):
-    """(ms of the FP8 attention kernel alone, ms of quantise Q + quantise K + attention)."""
+    """(ms of the FP8 attention kernel alone, ms of quantise Q + quantise K + attention,
+    launch_spread of the attention kernel)."""
     from flashattention_forward_attn_amd import inputs
     w = x.workload
     q, k, v, lim = device_inputs(torch, x)
@@ -267,9 +271,10 @@ def measure_fp8(torch, binding, x, steps, warmup):
         attend()
 
     ms = time_launches(torch, attend, steps, warmup)
+    spread = launch_spread(torch, attend, SPREAD_LAUNCHES)
     ms_whole = time_launches(torch, whole, max(10, steps // 2), max(5, warmup // 4))
     del q, k, v, lim, signs, qc, qe, kc, ke, o, lse
-    return ms, ms_whole
+    return ms, ms_whole, spread
 
 
 def cpu_baseline_fp8(x, target_seconds: float):
@@ -300,9 +305,12 @@ def cpu_baseline_fp8(x, target_seconds: float):
 
 def fp8_entry(torch, binding, x, steps, warmup, traffic_file, cpu: bool, cpu_seconds: float):
     w = x.workload
-    ms, ms_whole = measure_fp8(torch, binding, x, steps, warmup)
+    ms, ms_whole, spread = measure_fp8(torch, binding, x, steps, warmup)
     tf = w.flops() / (ms * 1e-3) / 1e12
+    spread["TFLOP/s_at_median"] = round(w.flops() / (spread["median_ms"] * 1e-3) / 1e12, 2)
+    spread["TFLOP/s_at_min"] = round(w.flops() / (spread["min_ms"] * 1e-3) / 1e12, 2)
     entry = {"metric": FP8_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+             "per_launch": spread,
              "with_quantisation": {"ms_per_step": round(ms_whole, 5),
                                    "TFLOP/s": round(w.flops() / (ms_whole * 1e-3) / 1e12, 2)},
              "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_FP8_MIXED_TFLOPS, 1),
@@ -444,7 +452,7 @@ def main() -> int:
                 "config": {"workload": xd.workload.name, "B": xd.workload.B, "H": xd.workload.H, "d": xd.workload.d,
                            "max_len": xd.workload.max_len, "page": 16, "path": "decode",
                            "bytes_per_step": entry["bytes_per_step"], "parallelism": "single GPU"},
-                "roofline": entry["roofline"]}
+                "roofline": entry["roofline"], "per_launch": entry["per_launch"]}
         if "cpu_baseline" in entry:
             line["cpu_baseline"] = entry["cpu_baseline"]
         print(json.dumps(line), flush=True)
@@ -461,7 +469,8 @@ def main() -> int:
                 "data": "synthetic (seeded numpy draws, inputs resident in HBM)",
                 "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                            "path": "fp8", "flops_per_step": w.flops(), "parallelism": "single GPU"},
-                "roofline": entry["roofline"], "with_quantisation": entry["with_quantisation"]}
+                "roofline": entry["roofline"], "with_quantisation": entry["with_quantisation"],
+                "per_launch": entry["per_launch"]}
         if "cpu_baseline" in entry:
             line["cpu_baseline"] = entry["cpu_baseline"]
         print(json.dumps(line), flush=True)
