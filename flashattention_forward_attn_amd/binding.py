@@ -96,21 +96,77 @@ def _stream(stream) -> Optional[int]:
 
 
 def _dims(q):
-    if q.dim() != 4:
+    if not hasattr(q, "dim") or q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d] tensors")
     return tuple(int(x) for x in q.shape)
 
 
+# Every tensor argument is checked before its address is handed to the library:
+# the kernels read and write exactly the documented number of contiguous
+# elements of the documented type in device memory, so anything else would make
+# them touch memory the caller did not mean.
+
+def _expect(t, name: str, dtype, shape) -> None:
+    """dtype, shape and contiguity of one tensor argument."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_one_gpu(**tensors) -> None:
+    """All given tensors (None skipped) live on the same GPU."""
+    first = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+        if first is None:
+            first = t.device
+        elif t.device != first:
+            raise ValueError(f"{name} is on {t.device} but the other arguments are on {first}")
+
+
+def _workspace(ws) -> int:
+    """Byte size of a workspace tensor (contiguous uint8), 0 for None."""
+    import torch
+    if ws is None:
+        return 0
+    _expect(ws, "workspace", torch.uint8, ws.shape)
+    return ws.numel()
+
+
+def _forward_args(q, k, v, o, lse, kv_limit, dtype):
+    import torch
+    B, H, N, d = _dims(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(t, name, dtype, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if kv_limit is not None:
+        _expect(kv_limit, "kv_limit", torch.int32, (B, N))
+    return B, H, N, d
+
+
 def fa_fwd_bf16(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, stream=None) -> None:
     """Fused forward, bf16 tensors [B, H, N, d]; lse fp32 [B, H, N]; kv_limit int32 [B, N] or None."""
-    B, H, N, d = _dims(q)
+    import torch
+    B, H, N, d = _forward_args(q, k, v, o, lse, kv_limit, torch.bfloat16)
+    _on_one_gpu(q=q, k=k, v=v, o=o, lse=lse, kv_limit=kv_limit)
     _check(load().fa_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
                               float(scale), _ptr(kv_limit), _stream(stream)))
 
 
 def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, stream=None) -> None:
     """Fused forward, fp32 tensors [B, H, N, d]."""
-    B, H, N, d = _dims(q)
+    import torch
+    B, H, N, d = _forward_args(q, k, v, o, lse, kv_limit, torch.float32)
+    _on_one_gpu(q=q, k=k, v=v, o=o, lse=lse, kv_limit=kv_limit)
     _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
                              float(scale), _ptr(kv_limit), _stream(stream)))
 
@@ -122,8 +178,10 @@ def fa_unfused_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
 def fa_fwd_unfused_bf16(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, workspace=None,
                         stream=None) -> None:
     """Unfused three-kernel forward (bf16); workspace is a device uint8 tensor."""
-    B, H, N, d = _dims(q)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    import torch
+    B, H, N, d = _forward_args(q, k, v, o, lse, kv_limit, torch.bfloat16)
+    nbytes = _workspace(workspace)
+    _on_one_gpu(q=q, k=k, v=v, o=o, lse=lse, kv_limit=kv_limit, workspace=workspace)
     _check(load().fa_fwd_unfused_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                       int(bool(causal)), float(scale), _ptr(kv_limit), _ptr(workspace), nbytes,
                                       _stream(stream)))
@@ -132,8 +190,10 @@ def fa_fwd_unfused_bf16(q, k, v, o, lse, causal: bool, scale: float, kv_limit=No
 def fa_fwd_unfused_f32(q, k, v, o, lse, causal: bool, scale: float, kv_limit=None, workspace=None,
                        stream=None) -> None:
     """Unfused three-kernel forward (fp32)."""
-    B, H, N, d = _dims(q)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    import torch
+    B, H, N, d = _forward_args(q, k, v, o, lse, kv_limit, torch.float32)
+    nbytes = _workspace(workspace)
+    _on_one_gpu(q=q, k=k, v=v, o=o, lse=lse, kv_limit=kv_limit, workspace=workspace)
     _check(load().fa_fwd_unfused_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      int(bool(causal)), float(scale), _ptr(kv_limit), _ptr(workspace), nbytes,
                                      _stream(stream)))
@@ -147,8 +207,13 @@ def fa_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float, k
                 stream=None) -> None:
     """Backward pass of fa_fwd_bf16: bf16 [B, H, N, d] tensors, lse fp32 [B, H, N]; workspace a device
     uint8 tensor of at least fa_bwd_workspace_bytes(B, H, N) bytes."""
-    B, H, N, d = _dims(q)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    import torch
+    B, H, N, d = _forward_args(q, k, v, o, lse, kv_limit, torch.bfloat16)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    nbytes = _workspace(workspace)
+    _on_one_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, kv_limit=kv_limit,
+                workspace=workspace)
     _check(load().fa_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit),
                               _ptr(workspace), nbytes, _stream(stream)))
@@ -179,12 +244,23 @@ def fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, sca
     """Decode over a paged cache: q, o bf16 [B, H, d]; k_cache, v_cache bf16 [num_pages, H, 16, d];
     block_table int32 [B, max_pages]; seq_lens int32 [B]; lse fp32 [B, H]; workspace a device uint8
     tensor of at least fa_decode_workspace_bytes(B, H, d, max_pages) bytes."""
-    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
+    import torch
+    if not all(hasattr(t, "dim") for t in (q, k_cache, block_table)) or q.dim() != 3 or k_cache.dim() != 4 \
+            or block_table.dim() != 2:
         raise ValueError("q must be [B, H, d], the caches [num_pages, H, page_size, d], block_table [B, max_pages]")
     B, H, d = (int(x) for x in q.shape)
     num_pages, _, page_size, _ = (int(x) for x in k_cache.shape)
     max_pages = int(block_table.shape[1])
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _expect(q, "q", torch.bfloat16, (B, H, d))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _expect(t, name, torch.bfloat16, (num_pages, H, page_size, d))
+    _expect(block_table, "block_table", torch.int32, (B, max_pages))
+    _expect(seq_lens, "seq_lens", torch.int32, (B,))
+    _expect(o, "o", torch.bfloat16, (B, H, d))
+    _expect(lse, "lse", torch.float32, (B, H))
+    nbytes = _workspace(workspace)
+    _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, o=o, lse=lse,
+                workspace=workspace)
     _check(load().fa_decode_paged_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                        _ptr(o), _ptr(lse), B, H, d, page_size, max_pages, num_pages, float(scale),
                                        _ptr(workspace), nbytes, _stream(stream)))
@@ -212,7 +288,15 @@ FP8_Q_TILE, FP8_K_TILE = 32, 64
 def fa_fp8_quantize_bf16(x, signs, codes, exps, tile_rows: int, stream=None) -> None:
     """Rotate (signs, Hadamard) and encode a bf16 [B, H, N, d] tensor: codes uint8 [B, H, N, d],
     exps int32 [B, H, ceil(N / tile_rows)]; tile_rows 32 for q, 64 for k."""
+    import torch
     B, H, N, d = _dims(x)
+    if tile_rows not in (FP8_Q_TILE, FP8_K_TILE):
+        raise ValueError(f"tile_rows must be {FP8_Q_TILE} or {FP8_K_TILE}, got {tile_rows}")
+    _expect(x, "x", torch.bfloat16, (B, H, N, d))
+    _expect(signs, "signs", torch.int8, (d,))
+    _expect(codes, "codes", torch.uint8, (B, H, N, d))
+    _expect(exps, "exps", torch.int32, (B, H, -(-N // tile_rows)))
+    _on_one_gpu(x=x, signs=signs, codes=codes, exps=exps)
     _check(load().fa_fp8_quantize_bf16(_ptr(x), _ptr(signs), _ptr(codes), _ptr(exps), B, H, N, d, int(tile_rows),
                                        _stream(stream)))
 
@@ -220,7 +304,19 @@ def fa_fp8_quantize_bf16(x, signs, codes, exps, tile_rows: int, stream=None) -> 
 def fa_fwd_fp8(q_codes, q_exps, k_codes, k_exps, v, o, lse, causal: bool, scale: float, kv_limit=None,
                stream=None) -> None:
     """Fused forward on E4M3 q and k codes (from fa_fp8_quantize_bf16) and bf16 v."""
+    import torch
     B, H, N, d = _dims(v)
+    _expect(v, "v", torch.bfloat16, (B, H, N, d))
+    _expect(q_codes, "q_codes", torch.uint8, (B, H, N, d))
+    _expect(k_codes, "k_codes", torch.uint8, (B, H, N, d))
+    _expect(q_exps, "q_exps", torch.int32, (B, H, -(-N // FP8_Q_TILE)))
+    _expect(k_exps, "k_exps", torch.int32, (B, H, -(-N // FP8_K_TILE)))
+    _expect(o, "o", torch.bfloat16, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if kv_limit is not None:
+        _expect(kv_limit, "kv_limit", torch.int32, (B, N))
+    _on_one_gpu(q_codes=q_codes, q_exps=q_exps, k_codes=k_codes, k_exps=k_exps, v=v, o=o, lse=lse,
+                kv_limit=kv_limit)
     _check(load().fa_fwd_fp8(_ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v), _ptr(o), _ptr(lse),
                              B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit), _stream(stream)))
 
