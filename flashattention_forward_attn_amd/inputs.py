@@ -166,10 +166,17 @@ def custom(name: str, dtype: str, B: int, H: int, N: int, d: int, causal: bool, 
 
 def random_kv_limit(B: int, N: int, seed: int, kind: str) -> np.ndarray:
     """Per-row key limits for mask sweeps: 'random' (each row uniform in [0, N]),
-    'zeros' (every row fully masked), 'some_zero' (random, with every fifth row 0)."""
+    'zeros' (every row fully masked), 'some_zero' (random, with every fifth row 0),
+    'out_of_range' (uniform in [-N, 2N], with the int32 extremes every seventh and
+    eleventh row: the API clamps negative limits to 0 and limits past N to N)."""
     rng = np.random.default_rng(seed)
     if kind == "zeros":
         return np.zeros((B, N), np.int32)
+    if kind == "out_of_range":
+        lim = rng.integers(-N, 2 * N + 1, size=(B, N)).astype(np.int32)
+        lim[:, ::7] = np.iinfo(np.int32).min
+        lim[:, 3::11] = np.iinfo(np.int32).max
+        return lim
     lim = rng.integers(0, N + 1, size=(B, N)).astype(np.int32)
     if kind == "some_zero":
         lim[:, ::5] = 0

@@ -86,7 +86,7 @@ def run_backward(x, g, kv_limit=None, given=None):
 SWEEP_N = [1, 5, 17, 64, 65, 130, 200, 257]
 
 
-@pytest.mark.parametrize("mask", ["none", "some_zero"])
+@pytest.mark.parametrize("mask", ["none", "some_zero", "out_of_range"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SWEEP_N)

@@ -78,7 +78,7 @@ def test_quantise_bit_exact(N, d, tile):
     np.testing.assert_array_equal(codes, rc)
 
 
-@pytest.mark.parametrize("mask", ["none", "some_zero"])
+@pytest.mark.parametrize("mask", ["none", "some_zero", "out_of_range"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 65, 130, 257])

@@ -2,7 +2,8 @@
 same seeded inputs, element by element.
 
   - an odd-size sweep: N from 1 to 257 across tile edges, d in {64, 128},
-    causal on and off, four key-limit patterns, fused and unfused;
+    causal on and off, five key-limit patterns (out-of-range limits included,
+    which the API clamps to [0, N]), fused and unfused;
   - the five workloads at full size: full oracle where it finishes in seconds,
     otherwise sampled rows (first and last rows, tile edges, the diagonal, the
     masked query block) plus properties over every row;
@@ -18,7 +19,7 @@ from tests import gpu_helpers as gh
 pytestmark = pytest.mark.gpu
 
 SWEEP_N = [1, 2, 3, 5, 16, 17, 63, 64, 65, 127, 128, 129, 200, 255, 257]
-MASKS = [None, "random", "some_zero", "zeros"]
+MASKS = [None, "random", "some_zero", "zeros", "out_of_range"]
 
 
 def _limits(kind, B, N, seed):
