@@ -69,7 +69,7 @@ typedef enum {
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                      */
     FA_ERR_SCALE = 4,     /* scale is NaN, infinite, zero or negative                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
-    FA_ERR_WORKSPACE = 6, /* unfused or backward path: workspace NULL, too small or misaligned */
+    FA_ERR_WORKSPACE = 6, /* unfused, backward or decode path: workspace NULL, too small or misaligned */
     FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch                */
     FA_ERR_ALIAS = 8      /* an output overlaps an input, the other output or the workspace */
 } fa_status;
