@@ -68,6 +68,8 @@ def open_library(path: str):
     lib.fa_fp8_quantize_bf16.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]
     lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8_qbf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd_fp8_qbf16.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     return lib
@@ -321,6 +323,26 @@ def fa_fwd_fp8(q_codes, q_exps, k_codes, k_exps, v, o, lse, causal: bool, scale:
                              B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit), _stream(stream)))
 
 
+def fa_fwd_fp8_qbf16(q, signs, k_codes, k_exps, v, o, lse, causal: bool, scale: float, kv_limit=None,
+                     stream=None) -> None:
+    """FP8 forward with q in bf16 (rotated and encoded inside the kernel, the same codes
+    fa_fp8_quantize_bf16 would store) and k as codes from fa_fp8_quantize_bf16."""
+    import torch
+    B, H, N, d = _dims(q)
+    _expect(q, "q", torch.bfloat16, (B, H, N, d))
+    _expect(signs, "signs", torch.int8, (d,))
+    _expect(k_codes, "k_codes", torch.uint8, (B, H, N, d))
+    _expect(k_exps, "k_exps", torch.int32, (B, H, -(-N // FP8_K_TILE)))
+    _expect(v, "v", torch.bfloat16, (B, H, N, d))
+    _expect(o, "o", torch.bfloat16, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if kv_limit is not None:
+        _expect(kv_limit, "kv_limit", torch.int32, (B, N))
+    _on_one_gpu(q=q, signs=signs, k_codes=k_codes, k_exps=k_exps, v=v, o=o, lse=lse, kv_limit=kv_limit)
+    _check(load().fa_fwd_fp8_qbf16(_ptr(q), _ptr(signs), _ptr(k_codes), _ptr(k_exps), _ptr(v), _ptr(o), _ptr(lse),
+                                   B, H, N, d, int(bool(causal)), float(scale), _ptr(kv_limit), _stream(stream)))
+
+
 def fp8_quantize(x, signs, tile_rows: int, stream=None):
     """Allocate and fill (codes, exps) for a bf16 tensor."""
     import torch
@@ -332,16 +354,16 @@ def fp8_quantize(x, signs, tile_rows: int, stream=None):
 
 
 def attention_fp8(q, k, v, signs, causal: bool = False, scale: Optional[float] = None, kv_limit=None, stream=None):
-    """FP8 forward from bf16 q, k, v: quantise q and k (same signs), then attention.  Returns (o, lse)."""
+    """FP8 forward from bf16 q, k, v: quantise k, then attention with q rotated and
+    encoded inside the kernel (the same signs for both).  Returns (o, lse)."""
     import torch
     B, H, N, d = _dims(q)
     if scale is None:
         scale = d ** -0.5
-    qc, qe = fp8_quantize(q, signs, FP8_Q_TILE, stream)
     kc, ke = fp8_quantize(k, signs, FP8_K_TILE, stream)
     o = torch.empty_like(v)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd_fp8(qc, qe, kc, ke, v, o, lse, causal, scale, kv_limit, stream)
+    fa_fwd_fp8_qbf16(q, signs, kc, ke, v, o, lse, causal, scale, kv_limit, stream)
     return o, lse
 
 

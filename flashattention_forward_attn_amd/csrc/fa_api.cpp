@@ -261,8 +261,31 @@ fa_status fa_fwd_fp8(const uint8_t* q_codes, const int32_t* q_exps, const uint8_
     for (Range in : ins)
         if (overlap(ro, in) || overlap(rl, in)) return FA_ERR_ALIAS;
     if (overlap(ro, rl)) return FA_ERR_ALIAS;
-    return hip_status(fa::launch_fused_fp8(q_codes, q_exps, k_codes, k_exps, v, o, lse, B, H, N, d, causal != 0,
-                                           scale, kv_limit, static_cast<hipStream_t>(stream)));
+    return hip_status(fa::launch_fused_fp8(q_codes, q_exps, nullptr, nullptr, k_codes, k_exps, v, o, lse, B, H, N, d,
+                                           causal != 0, scale, kv_limit, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8_qbf16(const fa_bf16* q, const int8_t* signs, const uint8_t* k_codes, const int32_t* k_exps,
+                           const fa_bf16* v, fa_bf16* o, float* lse, int B, int H, int N, int d, int causal,
+                           float scale, const int32_t* kv_limit, void* stream) {
+    if (!q || !signs || !k_codes || !k_exps || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
+    const int64_t elems = (int64_t)B * H * N * d;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(signs, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(k_exps, 4) || !aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4)))
+        return FA_ERR_ALIGN;
+    const int64_t nkt = (int64_t)B * H * ((N + fa::kFp8KTile - 1) / fa::kFp8KTile);
+    const Range ins[] = {span(q, elems * 2), span(signs, d), span(k_codes, elems), span(k_exps, nkt * 4),
+                         span(v, elems * 2), span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0)};
+    const Range ro = span(o, elems * 2), rl = span(lse, (int64_t)B * H * N * 4);
+    for (Range in : ins)
+        if (overlap(ro, in) || overlap(rl, in)) return FA_ERR_ALIAS;
+    if (overlap(ro, rl)) return FA_ERR_ALIAS;
+    return hip_status(fa::launch_fused_fp8(nullptr, nullptr, q, signs, k_codes, k_exps, v, o, lse, B, H, N, d,
+                                           causal != 0, scale, kv_limit, static_cast<hipStream_t>(stream)));
 }
 
 const char* fa_status_str(fa_status s) {

@@ -30,6 +30,7 @@ namespace fa {
 namespace fp8 {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int8_t i8x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- 1. quantise
 constexpr int kQuantThreads = 256;
@@ -150,9 +151,14 @@ struct Tile {
     static constexpr int kPerWaveV = (kBlocksV + kWaves - 1) / kWaves;
 };
 
-template <int D, bool CAUSAL, bool MASK>
+// QRAW: Q arrives in bf16 (Qb) with the rotation's signs, and each wave rotates
+// and encodes its own 32 rows -- exactly one Q tile -- in its prologue, with the
+// quantisation kernel's steps in the same order, so the codes and the exponent
+// are the ones that kernel would store.  Otherwise Q arrives as codes (Qc, Qe).
+template <int D, bool CAUSAL, bool MASK, bool QRAW>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, const uint8_t* __restrict__ Kc,
+void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, const bf16* __restrict__ Qb,
+                const int8_t* __restrict__ signs, const uint8_t* __restrict__ Kc,
                 const int32_t* __restrict__ Ke, const bf16* __restrict__ V, bf16* __restrict__ O,
                 float* __restrict__ LSE, int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
@@ -204,29 +210,106 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
     const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
     const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
     if (lane == 0) block_max[w] = wmax;
-
-    // Q codes of this lane's query: 32 bytes per 64 dims (k = 32 half .. +31)
-    i32x8 qf[D / 64];
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) {
-        if (qrow < N) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(Qc + ((size_t)bh * N + qrow) * D + 64 * kk + 32 * half);
-            const u32x4 lo = src[0], hi = src[1];
-            qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        } else {
-            qf[kk] = i32x8{};
-        }
-    }
-    // E8M0 block scale of this wave's Q tile (uniform)
-    const int wq = q0 / kQPW + w;
-    const int qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
     int kv_end = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
     const int ntiles = (kv_end + kBK - 1) / kBK;
+    // the first K/V tile's loads go out before Q is prepared, which hides their latency
+    if (ntiles > 0) dma_tile(0, 0);
+
+    // Q codes of this lane's query: 32 bytes per 64 dims (k = 32 half .. +31)
+    i32x8 qf[D / 64];
+    int qscale;  // E8M0 block scale of this wave's Q tile (uniform)
+    if constexpr (QRAW) {
+        // y = H (s * q) for this lane's dims 64 kk + 32 half + i (rows past N are zeros)
+        float y[D / 64][32];
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) {
+            const int base = 64 * kk + 32 * half;
+            const i8x16 s0 = *reinterpret_cast<const i8x16*>(signs + base);
+            const i8x16 s1 = *reinterpret_cast<const i8x16*>(signs + base + 16);
+#pragma unroll
+            for (int c8 = 0; c8 < 4; ++c8) {
+                bf16x8 x = bf16x8{};
+                if (qrow < N) x = *reinterpret_cast<const bf16x8*>(Qb + ((size_t)bh * N + qrow) * D + base + 8 * c8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = 8 * c8 + e;
+                    y[kk][t] = (float)x[e] * (float)(t < 16 ? s0[t] : s1[t - 16]);
+                }
+            }
+        }
+        // butterfly stages h = 1 .. 16 inside each 32-dim block of the lane
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    if (!(i & h)) {
+                        const float a = y[kk][i], b = y[kk][i + h];
+                        y[kk][i] = a + b;
+                        y[kk][i + h] = a - b;
+                    }
+        // stage h = 32 across the lane halves: one v_permlane32_swap hands every
+        // lane (lower, upper) = the values of lanes l mod 32 and l mod 32 + 32;
+        // the lower half keeps lower + upper, the upper half lower - upper
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const uint32_t u = __builtin_bit_cast(uint32_t, y[kk][i]);
+                const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                const float lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+                const float hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+                y[kk][i] = half ? lo - hi : lo + hi;
+            }
+        // stage h = 64 between the lane's two blocks (d = 128)
+        if constexpr (D == 128) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const float a = y[0][i], b = y[1][i];
+                y[0][i] = a + b;
+                y[1][i] = a - b;
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[kk][i]));
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+        const int e = tile_exponent(amax);
+        const float inv = __builtin_ldexpf(1.f, -e);  // exact power of two
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j] * inv, y[kk][4 * j + 1] * inv,
+                                                                       0, false);
+                wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j + 2] * inv, y[kk][4 * j + 3] * inv,
+                                                               (int)wv, true);
+                qf[kk][j] = (int)wv;
+            }
+        qscale = 127 + e;
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) {
+            if (qrow < N) {
+                const u32x4* src =
+                    reinterpret_cast<const u32x4*>(Qc + ((size_t)bh * N + qrow) * D + 64 * kk + 32 * half);
+                const u32x4 lo = src[0], hi = src[1];
+                qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            } else {
+                qf[kk] = i32x8{};
+            }
+        }
+        const int wq = q0 / kQPW + w;
+        qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
 
     // K (A of S^T = K Q^T): key col (+32 per slab), bytes 64 kk + 32 half .. +31,
     // i.e. chunks 4 kk + 2 half and 4 kk + 2 half + 1 of the key row.
@@ -256,7 +339,6 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
     float m_ref = -INFINITY, l_sum = 0.f;
     const int32_t* kexp = Ke + (size_t)bh * nkt;
 
-    if (ntiles > 0) dma_tile(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -368,13 +450,14 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
     }
 }
 
-template <int D, bool CAUSAL, bool MASK>
-hipError_t launch(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const bf16* v, bf16* o,
-                  float* lse, int B, int H, int N, float c, const int32_t* kv_limit, hipStream_t stream) {
+template <int D, bool CAUSAL, bool MASK, bool QRAW>
+hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const int8_t* signs, const uint8_t* kc,
+                  const int32_t* ke, const bf16* v, bf16* o, float* lse, int B, int H, int N, float c,
+                  const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const dim3 grid((unsigned)((long long)B * H * nqb));
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), 0, stream, qc, qe, kc, ke, v, o, lse, H, N,
-                       nqb, c, kv_limit);
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), grid, dim3(kThreads), 0, stream, qc, qe, qb, signs, kc, ke,
+                       v, o, lse, H, N, nqb, c, kv_limit);
     return hipGetLastError();
 }
 
@@ -399,17 +482,20 @@ hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* code
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const void* v,
-                            void* o, float* lse, int B, int H, int N, int d, bool causal, float scale,
-                            const int32_t* kv_limit, hipStream_t stream) {
+hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const void* q_bf16, const int8_t* signs,
+                            const uint8_t* kc, const int32_t* ke, const void* v, void* o, float* lse, int B, int H,
+                            int N, int d, bool causal, float scale, const int32_t* kv_limit, hipStream_t stream) {
     using namespace fp8;
+    const bf16* Qb = static_cast<const bf16*>(q_bf16);
     const bf16* Vb = static_cast<const bf16*>(v);
     bf16* Ob = static_cast<bf16*>(o);
     const float c = scale * kLog2e / (float)d;  // the rotation multiplies every score by d
     const bool mask = kv_limit != nullptr;
-#define FA_DISPATCH(DD, CC, MM)                                                                               \
-    if (d == DD && causal == CC && mask == MM)                                                                \
-        return launch<DD, CC, MM>(qc, qe, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream);
+    const bool raw = q_bf16 != nullptr;
+#define FA_DISPATCH(DD, CC, MM)                                                                                 \
+    if (d == DD && causal == CC && mask == MM)                                                                  \
+        return raw ? launch<DD, CC, MM, true>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream) \
+                   : launch<DD, CC, MM, false>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream);
     FA_DISPATCH(64, false, false)
     FA_DISPATCH(64, false, true)
     FA_DISPATCH(64, true, false)

@@ -47,8 +47,10 @@ hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* code
                                int d, int tile_rows, hipStream_t stream);
 
 // Fused forward with E4M3 Q and K codes (scores divided by d) and bf16 V.
-hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const uint8_t* kc, const int32_t* ke, const void* v,
-                            void* o, float* lse, int B, int H, int N, int d, bool causal, float scale,
-                            const int32_t* kv_limit, hipStream_t stream);
+// Q either as codes and tile exponents (qc, qe; q_bf16 == nullptr) or as bf16
+// with the rotation's signs (q_bf16, signs), rotated and encoded in the kernel.
+hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const void* q_bf16, const int8_t* signs,
+                            const uint8_t* kc, const int32_t* ke, const void* v, void* o, float* lse, int B, int H,
+                            int N, int d, bool causal, float scale, const int32_t* kv_limit, hipStream_t stream);
 
 }  // namespace fa

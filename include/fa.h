@@ -265,6 +265,20 @@ fa_status fa_fwd_fp8(const uint8_t *q_codes, const int32_t *q_exps, const uint8_
                      const fa_bf16 *v, fa_bf16 *o, float *lse, int B, int H, int N, int d, int causal, float scale,
                      const int32_t *kv_limit, void *stream);
 
+/*
+ * FP8 forward in one call for Q: the same result as fa_fp8_quantize_bf16 on q
+ * (tile_rows 32) followed by fa_fwd_fp8, bit for bit, but q is given in bf16
+ * with the rotation's signs, and each group of 32 query rows is rotated and
+ * encoded inside the attention kernel, so Q's codes never reach device memory
+ * (one launch and one pass over Q fewer).  K still comes as codes and
+ * exponents from fa_fp8_quantize_bf16 with tile_rows 64 and the same signs.
+ * q [B, H, N, d] bf16, 16-byte aligned; signs [d] int8 (+1 or -1), 16-byte
+ * aligned; the other arguments as for fa_fwd_fp8.  Errors as for fa_fwd_fp8.
+ */
+fa_status fa_fwd_fp8_qbf16(const fa_bf16 *q, const int8_t *signs, const uint8_t *k_codes, const int32_t *k_exps,
+                           const fa_bf16 *v, fa_bf16 *o, float *lse, int B, int H, int N, int d, int causal,
+                           float scale, const int32_t *kv_limit, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status s);
 

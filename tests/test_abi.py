@@ -213,6 +213,27 @@ def fwd8(lib, qc=CQ, qe=EQ, kc=CK, ke=EK, v=VF, o=OF, l=LF, B=2, H=3, N=100, d=1
     return lib.fa_fwd_fp8(qc, qe, kc, ke, v, o, l, B, H, N, d, causal, scale, m, None)
 
 
+def fwd8q(lib, q=XQ, sg=SG, kc=CK, ke=EK, v=VF, o=OF, l=LF, B=2, H=3, N=100, d=128, causal=0, scale=0.125, m=None):
+    return lib.fa_fwd_fp8_qbf16(q, sg, kc, ke, v, o, l, B, H, N, d, causal, scale, m, None)
+
+
+def test_fp8_qbf16_validation(lib):
+    assert fwd8q(lib, q=None) == 1
+    assert fwd8q(lib, sg=None) == 1
+    assert fwd8q(lib, ke=None) == 1
+    assert fwd8q(lib, N=0) == 2
+    assert fwd8q(lib, B=1, H=1, N=1 << 24, d=128) == 2      # one head past 4 GiB
+    assert fwd8q(lib, d=96) == 3
+    assert fwd8q(lib, scale=float("nan")) == 4
+    assert fwd8q(lib, q=XQ + 8) == 5
+    assert fwd8q(lib, sg=SG + 8) == 5          # signs are read 16 bytes at a time
+    assert fwd8q(lib, kc=CK + 4) == 5
+    assert fwd8q(lib, l=LF + 2) == 5
+    assert fwd8q(lib, o=XQ) == 8               # output over q
+    assert fwd8q(lib, o=SG) == 8               # output over the signs
+    assert fwd8q(lib, l=OF + 64) == 8          # lse over the output
+
+
 def test_fp8_validation(lib):
     assert quant(lib, sg=None) == 1
     assert quant(lib, e=None) == 1

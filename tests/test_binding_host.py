@@ -88,3 +88,17 @@ def test_fp8_checks():
         binding.fa_fwd_fp8(codes, exps, codes, exps, x, bf(B, H, N, D), torch.zeros(B, H, N), False, 0.125)
     with pytest.raises(ValueError, match="q_codes must be a GPU tensor"):
         binding.fa_fwd_fp8(codes, exps, codes, ke, x, bf(B, H, N, D), torch.zeros(B, H, N), False, 0.125)
+
+
+def test_fp8_qbf16_checks():
+    q = bf(B, H, N, D)
+    signs = torch.ones(D, dtype=torch.int8)
+    kc = torch.zeros(B, H, N, D, dtype=torch.uint8)
+    ke = torch.zeros(B, H, 1, dtype=torch.int32)                         # ceil(40 / 64)
+    out = (bf(B, H, N, D), torch.zeros(B, H, N))
+    with pytest.raises(TypeError, match="signs must be"):
+        binding.fa_fwd_fp8_qbf16(q, signs.to(torch.int32), kc, ke, q, *out, False, 0.125)
+    with pytest.raises(ValueError, match="k_exps must have shape"):
+        binding.fa_fwd_fp8_qbf16(q, signs, kc, torch.zeros(B, H, 2, dtype=torch.int32), q, *out, False, 0.125)
+    with pytest.raises(ValueError, match="q must be a GPU tensor"):
+        binding.fa_fwd_fp8_qbf16(q, signs, kc, ke, q, *out, False, 0.125)

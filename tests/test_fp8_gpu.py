@@ -1,11 +1,15 @@
-"""GPU parity of the FP8 forward (fa_fp8_quantize_bf16 + fa_fwd_fp8) against the oracle.
+"""GPU parity of the FP8 forward (fa_fp8_quantize_bf16, fa_fwd_fp8, fa_fwd_fp8_qbf16)
+against the oracle.
 
   - quantisation is integer work: the GPU's E4M3 codes and tile exponents must
     equal the oracle's bit for bit (same fp32 butterfly order, same exponent
     rule, round to nearest even);
-  - attention: the GPU's o and lse from its own codes against the oracle's
-    attention on the oracle's codes, with the forward's bf16 tolerances (max
-    2e-2, mean 2e-3 on o; 2e-2 on lse; empty rows exact);
+  - attention (binding.attention_fp8: k quantised by the quantisation kernel,
+    q encoded inside the attention kernel): the GPU's o and lse against the
+    oracle's attention on the oracle's codes, with the forward's bf16
+    tolerances (max 2e-2, mean 2e-3 on o; 2e-2 on lse; empty rows exact);
+  - q encoded inside the attention kernel gives the same results, bit for bit,
+    as quantising q first and calling fa_fwd_fp8;
   - accuracy, the page's claim: on inputs with outlier features the GPU path's
     RMSE against exact attention is below that of FP8 with one scale per tensor
     and no rotation (computed by the oracle).
@@ -136,3 +140,64 @@ def test_fp8_workload_sampled(name):
                                    nthreads=oracle_threads())
     check(o[b, h, ids], lse[b, h, ids], ro, rl, name)
     assert np.all(np.isfinite(o))
+
+
+def two_ways(torch, q, k, v, signs, causal, scale, lim=None):
+    """(o, lse) of quantise-q + fa_fwd_fp8, and of fa_fwd_fp8_qbf16 (q encoded in the kernel)."""
+    qd, kd, vd = dev_bf16(torch, q), dev_bf16(torch, k), dev_bf16(torch, v)
+    sd = torch.from_numpy(signs).cuda()
+    lim_d = None if lim is None else torch.from_numpy(np.ascontiguousarray(lim, np.int32)).cuda()
+    qc, qe = binding.fp8_quantize(qd, sd, binding.FP8_Q_TILE)
+    kc, ke = binding.fp8_quantize(kd, sd, binding.FP8_K_TILE)
+    B, H, N, _ = q.shape
+    outs = []
+    for fused in (False, True):
+        o = torch.empty_like(vd)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=vd.device)
+        if fused:
+            binding.fa_fwd_fp8_qbf16(qd, sd, kc, ke, vd, o, lse, causal, scale, lim_d)
+        else:
+            binding.fa_fwd_fp8(qc, qe, kc, ke, vd, o, lse, causal, scale, lim_d)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    return outs
+
+
+def bits_equal(torch, a, b):
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(view), b.view(view))
+
+
+@pytest.mark.parametrize("mask", ["none", "some_zero"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 31, 33, 100, 257])
+def test_q_encoded_in_kernel_equals_two_steps(N, causal, d, mask):
+    """fa_fwd_fp8_qbf16 takes the quantisation kernel's steps in the same order, so
+    its results equal quantise-then-attend bit for bit (magnitudes spread over many
+    powers of two, an all-zero Q tile and outlier columns included)."""
+    torch = cuda()
+    r = np.random.default_rng(N + 3 * d)
+    q = inputs.bf16_round(r.standard_normal((2, 3, N, d)).astype(np.float32)
+                          * np.exp2(r.integers(-12, 12, size=(2, 3, N, 1))).astype(np.float32))
+    q[1, 2, : min(N, 32)] = 0.0
+    q8, k8, _ = inputs.outlier_qkv(1, 1, N, d, seed=N)
+    q[0, 0] = q8[0, 0]
+    k = inputs.bf16_round(r.standard_normal((2, 3, N, d)).astype(np.float32))
+    k[0, 0] = k8[0, 0]
+    v = inputs.bf16_round(r.standard_normal((2, 3, N, d)).astype(np.float32))
+    lim = None if mask == "none" else inputs.random_kv_limit(2, N, seed=N, kind=mask)
+    (o1, l1), (o2, l2) = two_ways(torch, q, k, v, inputs.fp8_signs(d, seed=N), causal, d ** -0.5, lim)
+    what = f"N={N} causal={causal} d={d} mask={mask}"
+    assert bits_equal(torch, o1, o2), f"{what}: O differs"
+    assert bits_equal(torch, l1, l2), f"{what}: LSE differs"
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_b2h32n4096d128", "bf16_keypad_b8h32n1024d128", "bf16_b4h16n2048d64"])
+def test_q_encoded_in_kernel_equals_two_steps_workload(name):
+    torch = cuda()
+    w = inputs.WORKLOADS[name]
+    x = inputs.generate(w)
+    (o1, l1), (o2, l2) = two_ways(torch, x.q, x.k, x.v, inputs.fp8_signs(w.d), w.causal, w.scale, x.kv_limit)
+    assert bits_equal(torch, o1, o2), f"{name}: O differs"
+    assert bits_equal(torch, l1, l2), f"{name}: LSE differs"

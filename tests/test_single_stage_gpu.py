@@ -2,7 +2,7 @@
 the same forward kernels built with one LDS stage (a tile is loaded only after
 every wave has finished reading the previous one), and its results must equal
 libfa.so's bit for bit -- on ragged sweeps and on full-size workloads, for the
-bf16 forward and the FP8 forward."""
+bf16 forward and the FP8 forward (Q given as codes or encoded in the kernel)."""
 import numpy as np
 import pytest
 
@@ -32,22 +32,31 @@ def fwd_both(torch, libs, q, k, v, causal, scale, lim):
     return outs
 
 
-def fp8_both(torch, libs, q, k, v, causal, scale, lim):
+def fp8_both(torch, libs, q, k, v, causal, scale, lim, q_in_kernel=False):
     B, H, N, d = q.shape
     signs = torch.from_numpy(inputs.fp8_signs(d, seed=N)).cuda()
     qc, qe = binding.fp8_quantize(q, signs, binding.FP8_Q_TILE)
     kc, ke = binding.fp8_quantize(k, signs, binding.FP8_K_TILE)
     stream = torch.cuda.current_stream().cuda_stream
+    limp = None if lim is None else lim.data_ptr()
     outs = []
     for lib in libs:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-        assert lib.fa_fwd_fp8(qc.data_ptr(), qe.data_ptr(), kc.data_ptr(), ke.data_ptr(), v.data_ptr(),
-                              o.data_ptr(), lse.data_ptr(), B, H, N, d, int(causal), scale,
-                              None if lim is None else lim.data_ptr(), stream) == 0
+        if q_in_kernel:
+            st = lib.fa_fwd_fp8_qbf16(q.data_ptr(), signs.data_ptr(), kc.data_ptr(), ke.data_ptr(), v.data_ptr(),
+                                      o.data_ptr(), lse.data_ptr(), B, H, N, d, int(causal), scale, limp, stream)
+        else:
+            st = lib.fa_fwd_fp8(qc.data_ptr(), qe.data_ptr(), kc.data_ptr(), ke.data_ptr(), v.data_ptr(),
+                                o.data_ptr(), lse.data_ptr(), B, H, N, d, int(causal), scale, limp, stream)
+        assert st == 0
         outs.append((o, lse))
     torch.cuda.synchronize()
     return outs
+
+
+def fp8q_both(torch, libs, q, k, v, causal, scale, lim):
+    return fp8_both(torch, libs, q, k, v, causal, scale, lim, q_in_kernel=True)
 
 
 def same(outs, what):
@@ -62,7 +71,7 @@ def torch_equal(a, b):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-@pytest.mark.parametrize("path", ["bf16", "fp8"])
+@pytest.mark.parametrize("path", ["bf16", "fp8", "fp8q"])
 @pytest.mark.parametrize("mask", ["none", "random"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -75,16 +84,16 @@ def test_sweep(libs, N, causal, d, mask, path):
     lim = None
     if mask == "random":
         lim = torch.from_numpy(inputs.random_kv_limit(w.B, w.N, seed=N, kind="random")).cuda()
-    run = fwd_both if path == "bf16" else fp8_both
+    run = {"bf16": fwd_both, "fp8": fp8_both, "fp8q": fp8q_both}[path]
     same(run(torch, libs, q, k, v, causal, w.scale, lim), f"{path} N={N} causal={causal} d={d} mask={mask}")
 
 
-@pytest.mark.parametrize("path", ["bf16", "fp8"])
+@pytest.mark.parametrize("path", ["bf16", "fp8", "fp8q"])
 @pytest.mark.parametrize("name", ["bf16_causal_b2h32n4096d128", "bf16_keypad_b8h32n1024d128", "bf16_b4h16n2048d64"])
 def test_workload(libs, name, path):
     torch = cuda()
     x = inputs.generate(inputs.WORKLOADS[name])
     q, k, v, lim = to_device(x)
     w = x.workload
-    run = fwd_both if path == "bf16" else fp8_both
+    run = {"bf16": fwd_both, "fp8": fp8_both, "fp8q": fp8q_both}[path]
     same(run(torch, libs, q, k, v, w.causal, w.scale, lim), f"{path} {name}")
