@@ -408,8 +408,11 @@ struct Tile {
     static_assert(kBlocks % kWaves == 0, "tile must split evenly over the waves");
 };
 
+// At d = 64 the kernel fits in 128 registers, so two workgroups share a CU
+// (four waves per SIMD); at d = 128 it needs two waves' worth.
 template <int D, bool CAUSAL, bool MASK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2)))
 void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
             const bf16* __restrict__ dO, const float* __restrict__ Dd, const float* __restrict__ L2,
             bf16* __restrict__ dQ, int H, int N, int nqb, float c, float scale, const int32_t* __restrict__ kv_limit) {
