@@ -185,6 +185,17 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         *reinterpret_cast<const bf16x8*>(Sb + sub * 32 * T::kRow + koff[kk]), qf[kk], s[sub], 0, 0,
                         0);
+            // Schedule: the K operand reads run two MFMA pairs ahead of their use
+            // (left to itself the compiler issues them one pair ahead, and the
+            // products wait on LDS).  Groups: 4 LDS reads, then (2 MFMAs, 2 LDS
+            // reads) repeated, then the last 4 MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int g = 0; g < D / 16 - 2; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)

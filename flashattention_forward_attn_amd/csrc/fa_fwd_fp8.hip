@@ -365,6 +365,16 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                     s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0, kscale, 0,
                                                                               qscale);
                 }
+            // Schedule: the K operand reads run one product ahead of their use.
+            // Groups: 4 LDS reads, then (1 MFMA, 2 LDS reads) repeated, then the
+            // last 2 MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int g = 0; g < 2 * (D / 64) - 2; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
