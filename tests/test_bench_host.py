@@ -40,3 +40,14 @@ def test_traffic_reported_only_for_current_sources(tmp_path):
     assert bench.load_traffic(str(f), "decode", "w_good") is None
     assert bench.load_traffic(str(tmp_path / "absent.json"), "fused", "w_good") is None
 
+
+
+def test_unfused_bytes():
+    """S (fp32) and P (bf16) written and read once per head: 12 N^2 bytes, plus
+    Q, K, V, O (8 N d) and the fp32 LSE, when N is a multiple of 64."""
+    from flashattention_forward_attn_amd import inputs
+    w = inputs.WORKLOADS["bf16_causal_b2h32n4096d128"]
+    heads = w.B * w.H
+    assert bench.unfused_bytes(w) == heads * (12 * w.N ** 2 + 8 * w.N * w.d + 4 * w.N)
+    odd = inputs.custom("odd", "f32", 1, 1, 100, 64, False)        # rows padded to 128 keys, fp32 P
+    assert bench.unfused_bytes(odd) == 100 * 128 * 16 + 4 * 100 * 64 * 4 + 100 * 4
