@@ -551,7 +551,10 @@ def main() -> int:
         line["roofline"]["note"] = BWD_NOTE
     if not args.no_extras and args.path == "fused":
         ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
+        ugbs = unfused_bytes(w) / (ums * 1e-3) / 1e9
         line["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
+                           "GB/s": round(ugbs, 1), "hbm_frac": round(ugbs / PEAK_HBM_GBS, 4),
+                           "traffic": load_traffic(args.traffic, "unfused", w.name),
                            "fused_speedup": round(ums / ms, 2)}
         others = {}
         for name, ow in inputs.WORKLOADS.items():
