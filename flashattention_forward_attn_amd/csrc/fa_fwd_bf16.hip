@@ -58,12 +58,16 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = 32;                  // query rows per wave
 constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
-constexpr int kBK = 64;                   // keys per K/V tile
+// Keys per K/V tile: 128 at d = 64 (half the barriers per key; the tile fits
+// the registers there), 64 at d = 128.
+template <int D>
+constexpr int kBKof = D == 64 ? 128 : 64;
 constexpr float kStaleMax = 8.0f;         // log2 units
 
 template <int D>
 struct Tile {
     static constexpr int kRow = D * 2;              // bytes per key row
+    static constexpr int kBK = kBKof<D>;
     static constexpr int kBytes = kBK * kRow;       // one K or V tile
     static constexpr int kStage = 2 * kBytes;       // K tile then V tile
     static constexpr int kBlocks = kBytes / kDmaBytes;
@@ -78,6 +82,8 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                 bf16* __restrict__ O, float* __restrict__ LSE,
                 int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
+    constexpr int kBK = T::kBK;
+    constexpr int kSub = kBK / 32;  // 32-key slabs per tile
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[kWaves];
 
@@ -174,14 +180,14 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const int kv0 = t * kBK;
 
         if (kv0 < wmax) {
-            // S^T = K Q^T for two 32-key slabs; the two accumulator chains alternate
-            f32x16 s[2];
-            s[0] = f32x16{};
-            s[1] = f32x16{};
+            // S^T = K Q^T for kSub 32-key slabs; the slabs' accumulator chains alternate
+            f32x16 s[kSub];
+#pragma unroll
+            for (int i = 0; i < kSub; ++i) s[i] = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                for (int sub = 0; sub < kSub; ++sub)
                     s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         *reinterpret_cast<const bf16x8*>(Sb + sub * 32 * T::kRow + koff[kk]), qf[kk], s[sub], 0, 0,
                         0);
@@ -191,14 +197,14 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             // reads) repeated, then the last 4 MFMAs.
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int g = 0; g < D / 16 - 2; ++g) {
+            for (int g = 0; g < kSub * (D / 16) / 2 - 2; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -207,7 +213,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
+            for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
             mx = halves_max(mx);
@@ -225,10 +231,10 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
             // P = exp2(S c - m), packed to bf16; l sums the same rounded values
-            u32x4 pk[4];
+            u32x4 pk[kBK / 16];
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < kBK / 16; ++ks) {
                 const int sub = ks >> 1, base = (ks & 1) * 8;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
@@ -241,7 +247,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             }
             // O^T += V^T P^T; the D/32 accumulator chains alternate
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
                     const char* vb = Sb + 16 * ks * T::kRow;
@@ -251,6 +257,16 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                                                                         __builtin_bit_cast(bf16x8, pk[ks]),
                                                                         oacc[d32], 0, 0, 0);
                 }
+            if constexpr (D == 64) {
+                // V operand reads 8 ahead of their products
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+                for (int g = 0; g < D / 32 * (kBK / 16) - 4; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
         }
         if constexpr (kSingleStage) {
             __syncthreads();  // every wave has finished reading the stage
