@@ -127,7 +127,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = kFp8QTile;           // query rows per wave = one Q tile
 constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
-constexpr int kBK = kFp8KTile;            // keys per K/V tile = one K tile
+// keys per K/V tile: one K code tile at d = 128, two at d = 64 (each 64-key
+// half then takes its own exponent)
+template <int D>
+constexpr int kBKof = D == 64 ? 2 * kFp8KTile : kFp8KTile;
 constexpr float kStaleMax = 8.0f;         // log2 units
 
 // K rows of D E4M3 bytes: chunk c of row r sits in slot c ^ kswz(r), so that
@@ -140,6 +143,8 @@ __device__ __forceinline__ int kswz(int row) {
 
 template <int D>
 struct Tile {
+    static constexpr int kBK = kBKof<D>;
+    static constexpr int kSub = kBK / 32;           // 32-key slabs per tile
     static constexpr int kRowK = D;                 // E4M3 key row
     static constexpr int kRowV = 2 * D;             // bf16 value row
     static constexpr int kBytesK = kBK * kRowK;
@@ -162,6 +167,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                 const int32_t* __restrict__ Ke, const bf16* __restrict__ V, bf16* __restrict__ O,
                 float* __restrict__ LSE, int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
+    constexpr int kBK = T::kBK, kSub = T::kSub;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[kWaves];
 
@@ -175,7 +181,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
     const int bh = bid - qb * BHn;
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first over the whole grid
     const int b = bh / H;
-    const int nqt = (N + kQPW - 1) / kQPW, nkt = (N + kBK - 1) / kBK;
+    const int nqt = (N + kQPW - 1) / kQPW, nkt = (N + kFp8KTile - 1) / kFp8KTile;
 
     // Direct-to-LDS loads: block i * kWaves + w of the K tile and of the V tile.
     uint32_t koffd[T::kPerWaveK], voffd[T::kPerWaveV];
@@ -349,20 +355,26 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         const int kv0 = t * kBK;
 
         if (kv0 < wmax) {
-            const int kscale = 127 + kexp[t];
-            f32x16 s[2];
-            s[0] = f32x16{};
-            s[1] = f32x16{};
+            // E8M0 scale of each 64-key half (a half wholly past N has no code tile)
+            int kscale[kBK / kFp8KTile];
+#pragma unroll
+            for (int j = 0; j < kBK / kFp8KTile; ++j) {
+                const int kt = t * (kBK / kFp8KTile) + j;
+                kscale[j] = 127 + (kt < nkt ? kexp[kt] : 0);
+            }
+            f32x16 s[kSub];
+#pragma unroll
+            for (int sub = 0; sub < kSub; ++sub) s[sub] = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
+                for (int sub = 0; sub < kSub; ++sub) {
                     const char* kb = Sb + sub * 32 * T::kRowK;
                     const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + koff[kk][0]);
                     const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + koff[kk][1]);
                     const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0, kscale, 0,
+                    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0, kscale[sub / 2], 0,
                                                                               qscale);
                 }
             // Schedule: the K operand reads run one product ahead of their use.
@@ -370,14 +382,14 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
             // last 2 MFMAs.
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int g = 0; g < 2 * (D / 64) - 2; ++g) {
+            for (int g = 0; g < kSub * (D / 64) - 2; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -386,7 +398,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
+            for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
             mx = halves_max(mx);
@@ -403,10 +415,10 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
             }
             const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
-            u32x4 pk[4];
+            u32x4 pk[kBK / 16];
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < kBK / 16; ++ks) {
                 const int sub = ks >> 1, base = (ks & 1) * 8;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
@@ -418,7 +430,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                 }
             }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
                 for (int d32 = 0; d32 < D / 32; ++d32) {
                     const char* vb = Sb + 16 * ks * T::kRowV;

@@ -85,7 +85,7 @@ def test_quantise_bit_exact(N, d, tile):
 @pytest.mark.parametrize("mask", ["none", "some_zero", "out_of_range"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 65, 130, 257])
+@pytest.mark.parametrize("N", [1, 65, 130, 192, 257])
 def test_fp8_attention_sweep(N, causal, d, mask):
     torch = cuda()
     w = inputs.custom(f"fp8_n{N}", "bf16", 2, 2, N, d, causal, seed=N + d)
