@@ -42,11 +42,16 @@
 //     ragged tail and key padding).  A row that has seen no valid key keeps a
 //     finite exponent reference, so -inf - (-inf) is never formed
 //     ("07 GPU、资源估算与 FlashAttention" §7.8).
-//   * Workgroup order: query-block major, (batch, head) minor, and for causal
-//     attention the longest rows first over the whole grid (longest-processing-
-//     time-first, "FlashAttention 1–4 ...", section "FlashAttention-4").  With
-//     round-robin dispatch over the 8 XCDs, each XCD then sees a fixed subset
-//     of heads, and concurrently running workgroups read different heads.
+//   * Work order: query-block major, (batch, head) minor, and for causal
+//     attention the longest rows first (longest-processing-time-first,
+//     "FlashAttention 1–4 ...", section "FlashAttention-4").  Without a key
+//     limit one workgroup per CU walks the blocks: block g of every even round
+//     and the mirror image of g of every odd round, which evens out causal work
+//     (a long block pairs with a short one) and saves a workgroup launch and
+//     wind-down per block.  The mirror keeps g's residue mod 8, so with round-
+//     robin dispatch over the 8 XCDs each XCD still sees a fixed subset of
+//     heads.  With a key limit block lengths depend on the data, so every block
+//     gets its own workgroup and the hardware balances them.
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_tile.h"
@@ -80,25 +85,38 @@ template <int D, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ LSE,
-                int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
+                int H, int N, int nqb, int items, float c, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     constexpr int kBK = T::kBK;
     constexpr int kSub = kBK / 32;  // 32-key slabs per tile
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
-    __shared__ int block_max[kWaves];
+    __shared__ int block_max[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
-
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int BHn = G / nqb;
-    int qb = bid / BHn;
-    const int bh = bid - qb * BHn;
-    if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first over the whole grid
-    const int b = bh / H;
-    const size_t head = (size_t)bh * N * D;
+    const int P = gridDim.x, g = blockIdx.x;
+    const int BHn = items / nqb;
     const uint32_t head_bytes = (uint32_t)N * D * 2u;
+
+    // Item i is query block i / BHn of (batch, head) i mod BHn, the longest rows
+    // first for causal attention.  Workgroup g takes item g of rounds 0, 2, ...
+    // and, in rounds 1, 3, ..., the mirror image of g among the workgroups with
+    // its residue mod 8 (so it stays with the heads its XCD already holds).
+    auto item_of = [&](int r) -> int {
+        int j = g;
+        if (r & 1) j = (P & 7) ? P - 1 - g : P - 8 - (g & ~7) + (g & 7);
+        return r * P + j;
+    };
+    struct Item {
+        int bh, q0;
+    };
+    auto decode = [&](int it) -> Item {
+        int qb = it / BHn;
+        const int bh = it - qb * BHn;
+        if (CAUSAL) qb = nqb - 1 - qb;
+        return {bh, qb * kBQ};
+    };
 
     // Global offset (relative to the tile's first key) each lane fetches for its DMA blocks.
     uint32_t dma_off[T::kPerWave];
@@ -109,8 +127,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         dma_off[i] = (uint32_t)(row * T::kRow + 16 * (slot ^ swz<D>(row)));
     }
     // K/V tiles go to LDS with direct buffer loads (reads past N return zeros).
-    const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
-    auto dma_tile = [&](int stage, int kv0) {
+    auto dma_tile = [&](const i32x4& kdesc, const i32x4& vdesc, int stage, int kv0) __attribute__((always_inline)) {
         const uint32_t base = (uint32_t)kv0 * T::kRow;
 #pragma unroll
         for (int i = 0; i < T::kPerWave; ++i) {
@@ -119,28 +136,6 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             dma16(vdesc, kd + T::kBytes, base + dma_off[i]);
         }
     };
-
-    const int q0 = qb * kBQ;
-    const int qrow = q0 + w * kQPW + col;
-    const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
-    const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
-    if (lane == 0) block_max[w] = wmax;
-
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        if (qrow < N)
-            qf[kk] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
-        else
-            qf[kk] = bf16x8{};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) launder(qf[kk]);
-    int kv_end = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
-    const int ntiles = (kv_end + kBK - 1) / kBK;
 
     // LDS byte offsets of this lane's MFMA operands inside a stage.
     // K (A of S^T = K Q^T): key col (+32 per slab), chunk 2 kk + half.
@@ -164,139 +159,170 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         }
     }
 
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-    float m_ref = -INFINITY, l_sum = 0.f;
+    for (int r = 0, it = g; it < items; it = item_of(++r)) {
+        const Item cur = decode(it);
+        const int b = cur.bh / H;
+        const size_t head = (size_t)cur.bh * N * D;
+        const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
+        const int qrow = cur.q0 + w * kQPW + col;
+        const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
+        const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
+        // block_max alternates between two rows, so a fast wave writing the next
+        // item's entry never meets a slow wave still reading this one's
+        if (lane == 0) block_max[r & 1][w] = wmax;
 
-    if (ntiles > 0) dma_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+        bf16x8 qf[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            if (qrow < N)
+                qf[kk] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
+            else
+                qf[kk] = bf16x8{};
+        }
+        // after this barrier no wave reads the previous item's stages any more
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) launder(qf[kk]);
+        int kv_end = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[r & 1][i]);
+        const int ntiles = (kv_end + kBK - 1) / kBK;
+        if (ntiles > 0) dma_tile(kdesc, vdesc, 0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
 
-    auto step = [&](auto stage_c, int t) {
-        constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
-        if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
-        const char* Sb = smem + st * T::kStage;
-        const int kv0 = t * kBK;
+        f32x16 oacc[D / 32];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+        float m_ref = -INFINITY, l_sum = 0.f;
 
-        if (kv0 < wmax) {
-            // S^T = K Q^T for kSub 32-key slabs; the slabs' accumulator chains alternate
-            f32x16 s[kSub];
-#pragma unroll
-            for (int i = 0; i < kSub; ++i) s[i] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-                for (int sub = 0; sub < kSub; ++sub)
-                    s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8*>(Sb + sub * 32 * T::kRow + koff[kk]), qf[kk], s[sub], 0, 0,
-                        0);
-            // Schedule: the K operand reads run two MFMA pairs ahead of their use
-            // (left to itself the compiler issues them one pair ahead, and the
-            // products wait on LDS).  Groups: 4 LDS reads, then (2 MFMAs, 2 LDS
-            // reads) repeated, then the last 4 MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int g = 0; g < kSub * (D / 16) / 2 - 2; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
-#pragma unroll
-                for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        if (key >= lim) s[sub][r] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-            mx = halves_max(mx);
-            const float mt = mx * c;  // this tile's row max, log2 units
-            if (__any(mt > m_ref + kStaleMax)) {
-                const float m_new = fmaxf(m_ref, mt);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_sum *= alpha;
-#pragma unroll
-                for (int d32 = 0; d32 < D / 32; ++d32)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
-                m_ref = m_new;
-            }
-            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+        auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
+            constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
+            if (!kSingleStage && t + 1 < ntiles) dma_tile(kdesc, vdesc, st ^ 1, (t + 1) * kBK);
+            const char* Sb = smem + st * T::kStage;
+            const int kv0 = t * kBK;
 
-            // P = exp2(S c - m), packed to bf16; l sums the same rounded values
-            u32x4 pk[kBK / 16];
-            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            if (kv0 < wmax) {
+                // S^T = K Q^T for kSub 32-key slabs; the slabs' accumulator chains alternate
+                f32x16 s[kSub];
 #pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks) {
-                const int sub = ks >> 1, base = (ks & 1) * 8;
+                for (int i = 0; i < kSub; ++i) s[i] = f32x16{};
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float x0 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p], c, -m_use));
-                    const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
-                    const uint32_t wv = pack_bf16x2(x0, x1);
-                    pk[ks][p] = wv;
-                    l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
-                }
-            }
-            // O^T += V^T P^T; the D/32 accumulator chains alternate
+                for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks)
+                    for (int sub = 0; sub < kSub; ++sub)
+                        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            *reinterpret_cast<const bf16x8*>(Sb + sub * 32 * T::kRow + koff[kk]), qf[kk], s[sub],
+                            0, 0, 0);
+                // Schedule: the K operand reads run two MFMA pairs ahead of their use
+                // (left to itself the compiler issues them one pair ahead, and the
+                // products wait on LDS).  Groups: 4 LDS reads, then (2 MFMAs, 2 LDS
+                // reads) repeated, then the last 4 MFMAs.
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-                for (int d32 = 0; d32 < D / 32; ++d32) {
-                    const char* vb = Sb + 16 * ks * T::kRow;
-                    const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
-                    const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-                    oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                        __builtin_bit_cast(bf16x8, pk[ks]),
-                                                                        oacc[d32], 0, 0, 0);
-                }
-            if constexpr (D == 64) {
-                // V operand reads 8 ahead of their products
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-                for (int g = 0; g < D / 32 * (kBK / 16) - 4; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                for (int gg = 0; gg < kSub * (D / 16) / 2 - 2; ++gg) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            }
-        }
-        if constexpr (kSingleStage) {
-            __syncthreads();  // every wave has finished reading the stage
-            if (t + 1 < ntiles) dma_tile(0, (t + 1) * kBK);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
-    }
+                if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
+#pragma unroll
+                    for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) {
+                            const int key = kv0 + sub * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
+                            if (key >= lim) s[sub][rr] = -INFINITY;
+                        }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[sub][rr]);
+                mx = halves_max(mx);
+                const float mt = mx * c;  // this tile's row max, log2 units
+                if (__any(mt > m_ref + kStaleMax)) {
+                    const float m_new = fmaxf(m_ref, mt);
+                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_sum *= alpha;
+#pragma unroll
+                    for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) oacc[d32][rr] *= alpha;
+                    m_ref = m_new;
+                }
+                const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
-    // Epilogue: one division per row; each lane half summed its own keys.
-    const float l_tot = halves_sum(l_sum);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-        bf16* orow = O + head + (size_t)qrow * D;
+                // P = exp2(S c - m), packed to bf16; l sums the same rounded values
+                u32x4 pk[kBK / 16];
+                const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-        for (int d32 = 0; d32 < D / 32; ++d32)
+                for (int ks = 0; ks < kBK / 16; ++ks) {
+                    const int sub = ks >> 1, base = (ks & 1) * 8;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dim = 32 * d32 + 8 * g + 4 * half;
-                u32x2 out;
-                out.x = pack_bf16x2(oacc[d32][4 * g + 0] * inv, oacc[d32][4 * g + 1] * inv);
-                out.y = pack_bf16x2(oacc[d32][4 * g + 2] * inv, oacc[d32][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + dim) = out;
+                    for (int p = 0; p < 4; ++p) {
+                        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p], c, -m_use));
+                        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
+                        const uint32_t wv = pack_bf16x2(x0, x1);
+                        pk[ks][p] = wv;
+                        l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
+                    }
+                }
+                // O^T += V^T P^T; the D/32 accumulator chains alternate
+#pragma unroll
+                for (int ks = 0; ks < kBK / 16; ++ks)
+#pragma unroll
+                    for (int d32 = 0; d32 < D / 32; ++d32) {
+                        const char* vb = Sb + 16 * ks * T::kRow;
+                        const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
+                        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                        oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                            __builtin_bit_cast(bf16x8, pk[ks]),
+                                                                            oacc[d32], 0, 0, 0);
+                    }
+                if constexpr (D == 64) {
+                    // V operand reads 8 ahead of their products
+                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+                    for (int gg = 0; gg < D / 32 * (kBK / 16) - 4; ++gg) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                }
             }
-        if (half == 0)
-            LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+            if constexpr (kSingleStage) {
+                __syncthreads();  // every wave has finished reading the stage
+                if (t + 1 < ntiles) dma_tile(kdesc, vdesc, 0, (t + 1) * kBK);
+            }
+            if (t + 1 < ntiles) {  // after the last tile, the next item's first barrier serves
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+        }
+
+        // Epilogue: one division per row; each lane half summed its own keys.
+        const float l_tot = halves_sum(l_sum);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qrow < N) {
+            bf16* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+            for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int dim = 32 * d32 + 8 * gq + 4 * half;
+                    u32x2 out;
+                    out.x = pack_bf16x2(oacc[d32][4 * gq + 0] * inv, oacc[d32][4 * gq + 1] * inv);
+                    out.y = pack_bf16x2(oacc[d32][4 * gq + 2] * inv, oacc[d32][4 * gq + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + dim) = out;
+                }
+            if (half == 0)
+                LSE[(size_t)cur.bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+        }
     }
 }
 
@@ -304,9 +330,20 @@ template <int D, bool CAUSAL, bool MASK>
 hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse, int B, int H, int N,
                   float c, const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
-    const dim3 grid((unsigned)((long long)B * H * nqb));
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
-                       nqb, c, kv_limit);
+    const long long items = (long long)B * H * nqb;
+    // One workgroup per CU walks a balanced list of query blocks.  Key limits
+    // make block lengths data-dependent, so there every block gets its own
+    // workgroup and the hardware balances them.
+    long long P = items;
+    if (!MASK) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cus > 0 && cus < P) P = cus;
+    }
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3((unsigned)P), dim3(kThreads), 0, stream, q, k, v, o, lse,
+                       H, N, nqb, (int)items, c, kv_limit);
     return hipGetLastError();
 }
 
