@@ -331,19 +331,13 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* l
                   float c, const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const long long items = (long long)B * H * nqb;
-    // One workgroup per CU walks a balanced list of query blocks.  Key limits
-    // make block lengths data-dependent, so there every block gets its own
-    // workgroup and the hardware balances them.
-    long long P = items;
-    if (!MASK) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        if (cus > 0 && cus < P) P = cus;
-    }
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3((unsigned)P), dim3(kThreads), 0, stream, q, k, v, o, lse,
-                       H, N, nqb, (int)items, c, kv_limit);
+    // Key limits make block lengths data-dependent: there every block gets its
+    // own workgroup and the hardware balances them.
+    unsigned grid = 0;
+    const hipError_t e = forward_grid(items, !MASK, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
+                       nqb, (int)items, c, kv_limit);
     return hipGetLastError();
 }
 

@@ -165,22 +165,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, const bf16* __restrict__ Qb,
                 const int8_t* __restrict__ signs, const uint8_t* __restrict__ Kc,
                 const int32_t* __restrict__ Ke, const bf16* __restrict__ V, bf16* __restrict__ O,
-                float* __restrict__ LSE, int H, int N, int nqb, float c, const int32_t* __restrict__ kv_limit) {
+                float* __restrict__ LSE, int H, int N, int nqb, int items, float c,
+                const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     constexpr int kBK = T::kBK, kSub = T::kSub;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
-    __shared__ int block_max[kWaves];
+    __shared__ int block_max[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
 
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int BHn = G / nqb;
-    int qb = bid / BHn;
-    const int bh = bid - qb * BHn;
-    if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first over the whole grid
-    const int b = bh / H;
+    const int P = gridDim.x, g = blockIdx.x;
+    const int BHn = items / nqb;
+    // Query blocks in the bf16 kernel's order and walk: block g of rounds
+    // 0, 2, ... and the mirror image of g within its residue mod 8 in rounds
+    // 1, 3, ...; one block per workgroup when a key limit is given.
+    auto item_of = [&](int r) -> int {
+        int j = g;
+        if (r & 1) j = (P & 7) ? P - 1 - g : P - 8 - (g & ~7) + (g & 7);
+        return r * P + j;
+    };
     const int nqt = (N + kQPW - 1) / kQPW, nkt = (N + kFp8KTile - 1) / kFp8KTile;
 
     // Direct-to-LDS loads: block i * kWaves + w of the K tile and of the V tile.
@@ -197,278 +202,290 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         const int row = p / T::kRowV, slot = (p % T::kRowV) / 16;
         voffd[i] = (uint32_t)(row * T::kRowV + 16 * (slot ^ swz<D>(row)));
     }
-    const i32x4 kdesc = dma_desc(Kc + (size_t)bh * N * D, (uint32_t)N * D);
-    const i32x4 vdesc = dma_desc(V + (size_t)bh * N * D, (uint32_t)N * D * 2u);
-    auto dma_tile = [&](int stage, int kv0) __attribute__((always_inline)) {
-        const uint32_t st = lds_addr(smem + stage * T::kStage);
+    for (int r = 0, it = g; it < items; it = item_of(++r)) {
+        int qb = it / BHn;
+        const int bh = it - qb * BHn;
+        if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+        const int b = bh / H;
+        const i32x4 kdesc = dma_desc(Kc + (size_t)bh * N * D, (uint32_t)N * D);
+        const i32x4 vdesc = dma_desc(V + (size_t)bh * N * D, (uint32_t)N * D * 2u);
+        auto dma_tile = [&](int stage, int kv0) __attribute__((always_inline)) {
+            const uint32_t st = lds_addr(smem + stage * T::kStage);
 #pragma unroll
-        for (int i = 0; i < T::kPerWaveK; ++i)
-            if (i * kWaves + w < T::kBlocksK)
-                dma16(kdesc, st + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowK + koffd[i]);
+            for (int i = 0; i < T::kPerWaveK; ++i)
+                if (i * kWaves + w < T::kBlocksK)
+                    dma16(kdesc, st + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowK + koffd[i]);
 #pragma unroll
-        for (int i = 0; i < T::kPerWaveV; ++i)
-            if (i * kWaves + w < T::kBlocksV)
-                dma16(vdesc, st + T::kBytesK + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowV + voffd[i]);
-    };
+            for (int i = 0; i < T::kPerWaveV; ++i)
+                if (i * kWaves + w < T::kBlocksV)
+                    dma16(vdesc, st + T::kBytesK + (i * kWaves + w) * kDmaBytes, (uint32_t)kv0 * T::kRowV + voffd[i]);
+        };
 
-    const int q0 = qb * kBQ;
-    const int qrow = q0 + w * kQPW + col;
-    const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
-    const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
-    if (lane == 0) block_max[w] = wmax;
-    __syncthreads();
-    int kv_end = 0;
+        const int q0 = qb * kBQ;
+        const int qrow = q0 + w * kQPW + col;
+        const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
+        const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
+        // two rows, so consecutive blocks never share one; after this barrier no
+        // wave reads the previous block's stages any more
+        if (lane == 0) block_max[r & 1][w] = wmax;
+        __syncthreads();
+        int kv_end = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
-    const int ntiles = (kv_end + kBK - 1) / kBK;
-    // the first K/V tile's loads go out before Q is prepared, which hides their latency
-    if (ntiles > 0) dma_tile(0, 0);
+        for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[r & 1][i]);
+        const int ntiles = (kv_end + kBK - 1) / kBK;
+        // the first K/V tile's loads go out before Q is prepared, which hides their latency
+        if (ntiles > 0) dma_tile(0, 0);
 
-    // Q codes of this lane's query: 32 bytes per 64 dims (k = 32 half .. +31)
-    i32x8 qf[D / 64];
-    int qscale;  // E8M0 block scale of this wave's Q tile (uniform)
-    if constexpr (QRAW) {
-        // y = H (s * q) for this lane's dims 64 kk + 32 half + i (rows past N are zeros)
-        float y[D / 64][32];
+        // Q codes of this lane's query: 32 bytes per 64 dims (k = 32 half .. +31)
+        i32x8 qf[D / 64];
+        int qscale;  // E8M0 block scale of this wave's Q tile (uniform)
+        if constexpr (QRAW) {
+            // y = H (s * q) for this lane's dims 64 kk + 32 half + i (rows past N are zeros)
+            float y[D / 64][32];
 #pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk) {
-            const int base = 64 * kk + 32 * half;
-            const i8x16 s0 = *reinterpret_cast<const i8x16*>(signs + base);
-            const i8x16 s1 = *reinterpret_cast<const i8x16*>(signs + base + 16);
+            for (int kk = 0; kk < D / 64; ++kk) {
+                const int base = 64 * kk + 32 * half;
+                const i8x16 s0 = *reinterpret_cast<const i8x16*>(signs + base);
+                const i8x16 s1 = *reinterpret_cast<const i8x16*>(signs + base + 16);
 #pragma unroll
-            for (int c8 = 0; c8 < 4; ++c8) {
-                bf16x8 x = bf16x8{};
-                if (qrow < N) x = *reinterpret_cast<const bf16x8*>(Qb + ((size_t)bh * N + qrow) * D + base + 8 * c8);
+                for (int c8 = 0; c8 < 4; ++c8) {
+                    bf16x8 x = bf16x8{};
+                    if (qrow < N)
+                        x = *reinterpret_cast<const bf16x8*>(Qb + ((size_t)bh * N + qrow) * D + base + 8 * c8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = 8 * c8 + e;
-                    y[kk][t] = (float)x[e] * (float)(t < 16 ? s0[t] : s1[t - 16]);
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 8 * c8 + e;
+                        y[kk][t] = (float)x[e] * (float)(t < 16 ? s0[t] : s1[t - 16]);
+                    }
                 }
             }
-        }
-        // butterfly stages h = 1 .. 16 inside each 32-dim block of the lane
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-            for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    if (!(i & h)) {
-                        const float a = y[kk][i], b = y[kk][i + h];
-                        y[kk][i] = a + b;
-                        y[kk][i + h] = a - b;
-                    }
-        // stage h = 32 across the lane halves: one v_permlane32_swap hands every
-        // lane (lower, upper) = the values of lanes l mod 32 and l mod 32 + 32;
-        // the lower half keeps lower + upper, the upper half lower - upper
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                const uint32_t u = __builtin_bit_cast(uint32_t, y[kk][i]);
-                const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-                const float lo = __builtin_bit_cast(float, (uint32_t)r[0]);
-                const float hi = __builtin_bit_cast(float, (uint32_t)r[1]);
-                y[kk][i] = half ? lo - hi : lo + hi;
-            }
-        // stage h = 64 between the lane's two blocks (d = 128)
-        if constexpr (D == 128) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                const float a = y[0][i], b = y[1][i];
-                y[0][i] = a + b;
-                y[1][i] = a - b;
-            }
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[kk][i]));
-        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-        const int e = tile_exponent(amax);
-        const float inv = __builtin_ldexpf(1.f, -e);  // exact power of two
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j] * inv, y[kk][4 * j + 1] * inv,
-                                                                       0, false);
-                wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j + 2] * inv, y[kk][4 * j + 3] * inv,
-                                                               (int)wv, true);
-                qf[kk][j] = (int)wv;
-            }
-        qscale = 127 + e;
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk) {
-            if (qrow < N) {
-                const u32x4* src =
-                    reinterpret_cast<const u32x4*>(Qc + ((size_t)bh * N + qrow) * D + 64 * kk + 32 * half);
-                const u32x4 lo = src[0], hi = src[1];
-                qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            } else {
-                qf[kk] = i32x8{};
-            }
-        }
-        const int wq = q0 / kQPW + w;
-        qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
-    }
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
-
-    // K (A of S^T = K Q^T): key col (+32 per slab), bytes 64 kk + 32 half .. +31,
-    // i.e. chunks 4 kk + 2 half and 4 kk + 2 half + 1 of the key row.
-    int koff[D / 64][2];
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) koff[kk][j] = col * T::kRowK + 16 * ((4 * kk + 2 * half + j) ^ kswz<D>(col));
-    // V (A of O^T += V^T P^T) through ds_read_b64_tr_b16, as in the bf16 kernel.
-    int voff[D / 32][2];
-    {
-        const int G4 = lane >> 4, j = lane & 15;
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-            const int key = 8 * hs + 4 * (G4 >> 1) + (j >> 2);
-#pragma unroll
-            for (int d32 = 0; d32 < D / 32; ++d32) {
-                const int dim = 32 * d32 + 16 * (G4 & 1) + 4 * (j & 3);
-                voff[d32][hs] = T::kBytesK + key * T::kRowV + 16 * ((dim >> 3) ^ swz<D>(key)) + 2 * (dim & 7);
-            }
-        }
-    }
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-    float m_ref = -INFINITY, l_sum = 0.f;
-    const int32_t* kexp = Ke + (size_t)bh * nkt;
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
-        constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
-        if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
-        const char* Sb = smem + st * T::kStage;
-        const int kv0 = t * kBK;
-
-        if (kv0 < wmax) {
-            // E8M0 scale of each 64-key half (a half wholly past N has no code tile)
-            int kscale[kBK / kFp8KTile];
-#pragma unroll
-            for (int j = 0; j < kBK / kFp8KTile; ++j) {
-                const int kt = t * (kBK / kFp8KTile) + j;
-                kscale[j] = 127 + (kt < nkt ? kexp[kt] : 0);
-            }
-            f32x16 s[kSub];
-#pragma unroll
-            for (int sub = 0; sub < kSub; ++sub) s[sub] = f32x16{};
+            // butterfly stages h = 1 .. 16 inside each 32-dim block of the lane
 #pragma unroll
             for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
-                for (int sub = 0; sub < kSub; ++sub) {
-                    const char* kb = Sb + sub * 32 * T::kRowK;
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + koff[kk][0]);
-                    const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + koff[kk][1]);
-                    const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0, kscale[sub / 2], 0,
-                                                                              qscale);
-                }
-            // Schedule: the K operand reads run one product ahead of their use.
-            // Groups: 4 LDS reads, then (1 MFMA, 2 LDS reads) repeated, then the
-            // last 2 MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
-            for (int g = 0; g < kSub * (D / 64) - 2; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    for (int i = 0; i < 32; ++i)
+                        if (!(i & h)) {
+                            const float a = y[kk][i], b = y[kk][i + h];
+                            y[kk][i] = a + b;
+                            y[kk][i + h] = a - b;
+                        }
+            // stage h = 32 across the lane halves: one v_permlane32_swap hands every
+            // lane (lower, upper) = the values of lanes l mod 32 and l mod 32 + 32;
+            // the lower half keeps lower + upper, the upper half lower - upper
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const uint32_t u = __builtin_bit_cast(uint32_t, y[kk][i]);
+                    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                    const float lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+                    const float hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+                    y[kk][i] = half ? lo - hi : lo + hi;
+                }
+            // stage h = 64 between the lane's two blocks (d = 128)
+            if constexpr (D == 128) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const float a = y[0][i], b = y[1][i];
+                    y[0][i] = a + b;
+                    y[1][i] = a - b;
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
+            float amax = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[kk][i]));
+            for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+            const int e = tile_exponent(amax);
+            const float inv = __builtin_ldexpf(1.f, -e);  // exact power of two
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint32_t wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j] * inv, y[kk][4 * j + 1] * inv,
+                                                                           0, false);
+                    wv = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[kk][4 * j + 2] * inv, y[kk][4 * j + 3] * inv,
+                                                                   (int)wv, true);
+                    qf[kk][j] = (int)wv;
+                }
+            qscale = 127 + e;
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk) {
+                if (qrow < N) {
+                    const u32x4* src =
+                        reinterpret_cast<const u32x4*>(Qc + ((size_t)bh * N + qrow) * D + 64 * kk + 32 * half);
+                    const u32x4 lo = src[0], hi = src[1];
+                    qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                } else {
+                    qf[kk] = i32x8{};
+                }
+            }
+            const int wq = q0 / kQPW + w;
+            qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
+
+        // K (A of S^T = K Q^T): key col (+32 per slab), bytes 64 kk + 32 half .. +31,
+        // i.e. chunks 4 kk + 2 half and 4 kk + 2 half + 1 of the key row.
+        int koff[D / 64][2];
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) koff[kk][j] = col * T::kRowK + 16 * ((4 * kk + 2 * half + j) ^ kswz<D>(col));
+        // V (A of O^T += V^T P^T) through ds_read_b64_tr_b16, as in the bf16 kernel.
+        int voff[D / 32][2];
+        {
+            const int G4 = lane >> 4, j = lane & 15;
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const int key = 8 * hs + 4 * (G4 >> 1) + (j >> 2);
+#pragma unroll
+                for (int d32 = 0; d32 < D / 32; ++d32) {
+                    const int dim = 32 * d32 + 16 * (G4 & 1) + 4 * (j & 3);
+                    voff[d32][hs] = T::kBytesK + key * T::kRowV + 16 * ((dim >> 3) ^ swz<D>(key)) + 2 * (dim & 7);
+                }
+            }
+        }
+
+        f32x16 oacc[D / 32];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+        float m_ref = -INFINITY, l_sum = 0.f;
+        const int32_t* kexp = Ke + (size_t)bh * nkt;
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+
+        auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
+            constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
+            if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
+            const char* Sb = smem + st * T::kStage;
+            const int kv0 = t * kBK;
+
+            if (kv0 < wmax) {
+                // E8M0 scale of each 64-key half (a half wholly past N has no code tile)
+                int kscale[kBK / kFp8KTile];
+#pragma unroll
+                for (int j = 0; j < kBK / kFp8KTile; ++j) {
+                    const int kt = t * (kBK / kFp8KTile) + j;
+                    kscale[j] = 127 + (kt < nkt ? kexp[kt] : 0);
+                }
+                f32x16 s[kSub];
+#pragma unroll
+                for (int sub = 0; sub < kSub; ++sub) s[sub] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                    for (int sub = 0; sub < kSub; ++sub) {
+                        const char* kb = Sb + sub * 32 * T::kRowK;
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + koff[kk][0]);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + koff[kk][1]);
+                        const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], s[sub], 0, 0, 0,
+                                                                                  kscale[sub / 2], 0, qscale);
+                    }
+                // Schedule: the K operand reads run one product ahead of their use.
+                // Groups: 4 LDS reads, then (1 MFMA, 2 LDS reads) repeated, then the
+                // last 2 MFMAs.
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int g = 0; g < kSub * (D / 64) - 2; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (kv0 + kBK > wmin) {  // tile crosses some row's key limit
+#pragma unroll
+                    for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                            if (key >= lim) s[sub][r] = -INFINITY;
+                        }
+                }
+                float mx = -INFINITY;
 #pragma unroll
                 for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        if (key >= lim) s[sub][r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+                mx = halves_max(mx);
+                const float mt = mx * c;
+                if (__any(mt > m_ref + kStaleMax)) {
+                    const float m_new = fmaxf(m_ref, mt);
+                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_sum *= alpha;
+#pragma unroll
+                    for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
+                    m_ref = m_new;
+                }
+                const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+
+                u32x4 pk[kBK / 16];
+                const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+                for (int ks = 0; ks < kBK / 16; ++ks) {
+                    const int sub = ks >> 1, base = (ks & 1) * 8;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p], c, -m_use));
+                        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
+                        const uint32_t wv = pack_bf16x2(x0, x1);
+                        pk[ks][p] = wv;
+                        l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < kBK / 16; ++ks)
+#pragma unroll
+                    for (int d32 = 0; d32 < D / 32; ++d32) {
+                        const char* vb = Sb + 16 * ks * T::kRowV;
+                        const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
+                        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                        oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                            __builtin_bit_cast(bf16x8, pk[ks]),
+                                                                            oacc[d32], 0, 0, 0);
                     }
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-            mx = halves_max(mx);
-            const float mt = mx * c;
-            if (__any(mt > m_ref + kStaleMax)) {
-                const float m_new = fmaxf(m_ref, mt);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_sum *= alpha;
-#pragma unroll
-                for (int d32 = 0; d32 < D / 32; ++d32)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
-                m_ref = m_new;
+            if constexpr (kSingleStage) {
+                __syncthreads();  // every wave has finished reading the stage
+                if (t + 1 < ntiles) dma_tile(0, (t + 1) * kBK);
             }
-            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-            u32x4 pk[kBK / 16];
-            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks) {
-                const int sub = ks >> 1, base = (ks & 1) * 8;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float x0 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p], c, -m_use));
-                    const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
-                    const uint32_t wv = pack_bf16x2(x0, x1);
-                    pk[ks][p] = wv;
-                    l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
-                }
+            if (t + 1 < ntiles) {  // after the last tile, the next block's first barrier serves
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
             }
-#pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks)
-#pragma unroll
-                for (int d32 = 0; d32 < D / 32; ++d32) {
-                    const char* vb = Sb + 16 * ks * T::kRowV;
-                    const u32x2 lo = tr_read(vb + voff[d32][0]), hi = tr_read(vb + voff[d32][1]);
-                    const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-                    oacc[d32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                        __builtin_bit_cast(bf16x8, pk[ks]),
-                                                                        oacc[d32], 0, 0, 0);
-                }
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
         }
-        if constexpr (kSingleStage) {
-            __syncthreads();  // every wave has finished reading the stage
-            if (t + 1 < ntiles) dma_tile(0, (t + 1) * kBK);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
-    }
 
-    const float l_tot = halves_sum(l_sum);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-        bf16* orow = O + ((size_t)bh * N + qrow) * D;
+        const float l_tot = halves_sum(l_sum);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qrow < N) {
+            bf16* orow = O + ((size_t)bh * N + qrow) * D;
 #pragma unroll
-        for (int d32 = 0; d32 < D / 32; ++d32)
+            for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dim = 32 * d32 + 8 * g + 4 * half;
-                u32x2 out;
-                out.x = pack_bf16x2(oacc[d32][4 * g + 0] * inv, oacc[d32][4 * g + 1] * inv);
-                out.y = pack_bf16x2(oacc[d32][4 * g + 2] * inv, oacc[d32][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + dim) = out;
-            }
-        if (half == 0)
-            LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+                for (int g = 0; g < 4; ++g) {
+                    const int dim = 32 * d32 + 8 * g + 4 * half;
+                    u32x2 out;
+                    out.x = pack_bf16x2(oacc[d32][4 * g + 0] * inv, oacc[d32][4 * g + 1] * inv);
+                    out.y = pack_bf16x2(oacc[d32][4 * g + 2] * inv, oacc[d32][4 * g + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + dim) = out;
+                }
+            if (half == 0)
+                LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+        }
     }
 }
 
@@ -477,9 +494,12 @@ hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const in
                   const int32_t* ke, const bf16* v, bf16* o, float* lse, int B, int H, int N, float c,
                   const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
-    const dim3 grid((unsigned)((long long)B * H * nqb));
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), grid, dim3(kThreads), 0, stream, qc, qe, qb, signs, kc, ke,
-                       v, o, lse, H, N, nqb, c, kv_limit);
+    const long long items = (long long)B * H * nqb;
+    unsigned grid = 0;
+    const hipError_t e = forward_grid(items, !MASK, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), dim3(grid), dim3(kThreads), 0, stream, qc, qe, qb, signs,
+                       kc, ke, v, o, lse, H, N, nqb, (int)items, c, kv_limit);
     return hipGetLastError();
 }
 

@@ -10,6 +10,22 @@
 
 namespace fa {
 
+// Grid of a forward launch over `blocks` query blocks: with `walk`, one
+// workgroup per CU of the current device (never more than there are blocks),
+// each walking several blocks; otherwise one workgroup per block.
+inline hipError_t forward_grid(long long blocks, bool walk, unsigned* grid) {
+    long long n = blocks;
+    if (walk) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cus > 0 && cus < n) n = cus;
+    }
+    *grid = (unsigned)n;
+    return hipSuccess;
+}
+
 hipError_t launch_fused_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                              int N, int d, bool causal, float scale, const int32_t* kv_limit,
                              hipStream_t stream);
