@@ -159,7 +159,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         }
     }
 
-    for (int r = 0, it = g; it < items; it = item_of(++r)) {
+    for (int r = 0, it = g; it < items; it = MASK ? items : item_of(++r)) {
         const Item cur = decode(it);
         const int b = cur.bh / H;
         const size_t head = (size_t)cur.bh * N * D;
@@ -334,7 +334,7 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* l
     // Key limits make block lengths data-dependent: there every block gets its
     // own workgroup and the hardware balances them.
     unsigned grid = 0;
-    const hipError_t e = forward_grid(items, !MASK, &grid);
+    const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
                        nqb, (int)items, c, kv_limit);

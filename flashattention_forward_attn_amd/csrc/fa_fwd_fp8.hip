@@ -202,7 +202,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         const int row = p / T::kRowV, slot = (p % T::kRowV) / 16;
         voffd[i] = (uint32_t)(row * T::kRowV + 16 * (slot ^ swz<D>(row)));
     }
-    for (int r = 0, it = g; it < items; it = item_of(++r)) {
+    for (int r = 0, it = g; it < items; it = MASK ? items : item_of(++r)) {
         int qb = it / BHn;
         const int bh = it - qb * BHn;
         if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
@@ -496,7 +496,7 @@ hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const in
     const int nqb = (N + kBQ - 1) / kBQ;
     const long long items = (long long)B * H * nqb;
     unsigned grid = 0;
-    const hipError_t e = forward_grid(items, !MASK, &grid);
+    const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), dim3(grid), dim3(kThreads), 0, stream, qc, qe, qb, signs,
                        kc, ke, v, o, lse, H, N, nqb, (int)items, c, kv_limit);

@@ -12,8 +12,10 @@ namespace fa {
 
 // Grid of a forward launch over `blocks` query blocks: with `walk`, one
 // workgroup per CU of the current device (never more than there are blocks),
-// each walking several blocks; otherwise one workgroup per block.
-inline hipError_t forward_grid(long long blocks, bool walk, unsigned* grid) {
+// each walking several blocks; otherwise one workgroup per block.  Any grid
+// size covers every block exactly once, so the CU count only shapes the
+// schedule.
+inline hipError_t walk_grid(long long blocks, bool walk, unsigned* grid) {
     long long n = blocks;
     if (walk) {
         int dev = 0, cus = 0;
