@@ -100,14 +100,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     const uint32_t head_bytes = (uint32_t)N * D * 2u;
 
     // Item i is query block i / BHn of (batch, head) i mod BHn, the longest rows
-    // first for causal attention.  Workgroup g takes item g of rounds 0, 2, ...
-    // and, in rounds 1, 3, ..., the mirror image of g among the workgroups with
-    // its residue mod 8 (so it stays with the heads its XCD already holds).
-    auto item_of = [&](int r) -> int {
-        int j = g;
-        if (r & 1) j = (P & 7) ? P - 1 - g : P - 8 - (g & ~7) + (g & 7);
-        return r * P + j;
-    };
+    // first for causal attention; the grid walks the items with walk_block.
     struct Item {
         int bh, q0;
     };
@@ -159,7 +152,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         }
     }
 
-    for (int r = 0, it = g; it < items; it = MASK ? items : item_of(++r)) {
+    for (int r = 0, it = g; it < items; it = MASK ? items : walk_block(++r, g, P)) {
         const Item cur = decode(it);
         const int b = cur.bh / H;
         const size_t head = (size_t)cur.bh * N * D;

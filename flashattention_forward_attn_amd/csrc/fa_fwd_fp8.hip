@@ -178,14 +178,8 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
 
     const int P = gridDim.x, g = blockIdx.x;
     const int BHn = items / nqb;
-    // Query blocks in the bf16 kernel's order and walk: block g of rounds
-    // 0, 2, ... and the mirror image of g within its residue mod 8 in rounds
-    // 1, 3, ...; one block per workgroup when a key limit is given.
-    auto item_of = [&](int r) -> int {
-        int j = g;
-        if (r & 1) j = (P & 7) ? P - 1 - g : P - 8 - (g & ~7) + (g & 7);
-        return r * P + j;
-    };
+    // Query blocks in the bf16 kernel's order and walk (walk_block); one block
+    // per workgroup when a key limit is given.
     const int nqt = (N + kQPW - 1) / kQPW, nkt = (N + kFp8KTile - 1) / kFp8KTile;
 
     // Direct-to-LDS loads: block i * kWaves + w of the K tile and of the V tile.
@@ -202,7 +196,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         const int row = p / T::kRowV, slot = (p % T::kRowV) / 16;
         voffd[i] = (uint32_t)(row * T::kRowV + 16 * (slot ^ swz<D>(row)));
     }
-    for (int r = 0, it = g; it < items; it = MASK ? items : item_of(++r)) {
+    for (int r = 0, it = g; it < items; it = MASK ? items : walk_block(++r, g, P)) {
         int qb = it / BHn;
         const int bh = it - qb * BHn;
         if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first

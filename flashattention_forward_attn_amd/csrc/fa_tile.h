@@ -1,6 +1,6 @@
-// fa_tile.h -- LDS tile helpers shared by the bf16 kernels (forward and backward):
-// direct global -> LDS loads, the XOR chunk swizzle of a tile row, and the
-// transposing LDS read.
+// fa_tile.h -- helpers shared by the forward and backward kernels: direct
+// global -> LDS loads, the XOR chunk swizzle of a tile row, the transposing LDS
+// read, and the forward grids' walk over query blocks.
 #pragma once
 
 #include <type_traits>
@@ -89,6 +89,17 @@ __device__ __forceinline__ void dma4(const i32x4& desc, uint32_t dst, uint32_t v
 __device__ __forceinline__ u32x2 tr_read(const char* p) {
     const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
     return __builtin_bit_cast(u32x2, r);
+}
+
+// Block taken in round r by workgroup g of a grid of P that walks blocks
+// r P ... r P + P - 1 per round: block g in even rounds and, in odd rounds, the
+// mirror image of g among the workgroups with its residue mod 8 (round-robin
+// dispatch puts those on g's XCD), or among all when P is not a multiple of 8.
+// With blocks sorted longest first, a long block then pairs with a short one.
+__device__ __forceinline__ int walk_block(int r, int g, int P) {
+    int j = g;
+    if (r & 1) j = (P & 7) ? P - 1 - g : P - 8 - (g & ~7) + (g & 7);
+    return r * P + j;
 }
 
 }  // namespace fa
