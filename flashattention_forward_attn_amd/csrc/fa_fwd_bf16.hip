@@ -2,15 +2,15 @@
 //
 // The method: "GPU 与 TPU：让硬件不再是黑魔法" §11.2-§11.4 and "FlashAttention 1–4:
 // How IO-Awareness Reshaped the Attention Kernel", sections "FlashAttention (v1)"
-// and "FlashAttention-2".  One workgroup owns one block of query rows of one
-// (batch, head); it streams K/V tiles through LDS, keeps the score tile in
+// and "FlashAttention-2".  A workgroup owns one block of query rows of one
+// (batch, head) at a time; it streams K/V tiles through LDS, keeps the score tile in
 // matrix-core accumulators, and carries a running row max m, a running row sum
 // l and an unnormalised output accumulator, re-based whenever m moves; O is
 // divided by l once at the end and L = m + log l is written per row.  Scores
 // never reach device memory.
 //
 // gfx950 design (not the pages' A100/H100 tiling):
-//   * 8 waves x 32 query rows = 256 rows per workgroup, two waves per SIMD
+//   * 8 waves x 32 query rows = 256 rows per query block, two waves per SIMD
 //     (split-Q: each wave owns its rows outright, no cross-wave reduction,
 //     "FlashAttention 1–4 ...", section "FlashAttention-2", warp partitioning).
 //     Every K/V tile staged in LDS serves 256 queries.
@@ -62,7 +62,7 @@ namespace fused_bf16 {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = 32;                  // query rows per wave
-constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
+constexpr int kBQ = kWaves * kQPW;        // 256 query rows per query block
 // Keys per K/V tile: 128 at d = 64 (half the barriers per key; the tile fits
 // the registers there), 64 at d = 128.
 template <int D>

@@ -18,10 +18,11 @@
 //      the unnormalised Sylvester matrix (entries +-1), so scores carry a
 //      factor d, removed in the softmax scale.
 //   2. attention: the bf16 kernel's structure (8 waves x 32 query rows, K/V
-//      tiles of 64 keys by direct-to-LDS loads, transposed scores, bf16 P V)
-//      with S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands,
-//      and the two tiles' exponents passed as its E8M0 block scales, so the
-//      product comes out already scaled.  V stays bf16.
+//      tiles of 64 keys at d = 128 and 128 at d = 64 by direct-to-LDS loads,
+//      transposed scores, bf16 P V, the same walk over query blocks) with
+//      S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, and the
+//      two tiles' exponents passed as its E8M0 block scales, so the product
+//      comes out already scaled.  V stays bf16.
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_tile.h"
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __rest
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kQPW = kFp8QTile;           // query rows per wave = one Q tile
-constexpr int kBQ = kWaves * kQPW;        // 256 query rows per workgroup
+constexpr int kBQ = kWaves * kQPW;        // 256 query rows per query block
 // keys per K/V tile: one K code tile at d = 128, two at d = 64 (each 64-key
 // half then takes its own exponent)
 template <int D>
