@@ -54,7 +54,7 @@ fa_status validate(const void* q, const void* k, const void* v, const void* o, c
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!shape_ok(B, H, N, d, elem)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
         (kv_limit && !aligned(kv_limit, 4)))
         return FA_ERR_ALIGN;
@@ -164,7 +164,7 @@ fa_status fa_bwd_bf16(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, cons
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
     for (const void* p : {(const void*)q, (const void*)k, (const void*)v, (const void*)o, (const void*)dout,
                           (const void*)dq, (const void*)dk, (const void*)dv})
         if (!aligned(p, 16)) return FA_ERR_ALIGN;
@@ -200,7 +200,7 @@ fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const f
         (int64_t)B * H * 256 > (int64_t)UINT32_MAX)  // 256 threads per (sequence, head) in each launch
         return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
         !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
@@ -249,7 +249,7 @@ fa_status fa_fwd_fp8(const uint8_t* q_codes, const int32_t* q_exps, const uint8_
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
     if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(q_exps, 4) ||
         !aligned(k_exps, 4) || !aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4)))
         return FA_ERR_ALIGN;
@@ -273,7 +273,7 @@ fa_status fa_fwd_fp8_qbf16(const fa_bf16* q, const int8_t* signs, const uint8_t*
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!shape_ok(B, H, N, d, 2)) return FA_ERR_SHAPE;
     const int64_t elems = (int64_t)B * H * N * d;
-    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(signs, 16) || !aligned(k_codes, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(k_exps, 4) || !aligned(lse, 4) || (kv_limit && !aligned(kv_limit, 4)))
         return FA_ERR_ALIGN;
@@ -294,7 +294,7 @@ const char* fa_status_str(fa_status s) {
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "a size (B, H, N, pages, tile rows) is out of range";
         case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
-        case FA_ERR_SCALE: return "scale must be finite and positive";
+        case FA_ERR_SCALE: return "scale must be finite";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse and kv_limit 4-byte aligned";
         case FA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";

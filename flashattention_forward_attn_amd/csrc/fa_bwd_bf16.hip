@@ -97,7 +97,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
             const bf16* __restrict__ dO, const float* __restrict__ Dd, const float* __restrict__ L2,
             bf16* __restrict__ dK, bf16* __restrict__ dV, int H, int N, int nkb, float c, float scale,
-            const int32_t* __restrict__ kv_limit) {
+            uint32_t s_and, uint32_t s_xor, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(1024))) char smem[T::kSmem];
 
@@ -202,7 +202,11 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             if (kcol < N) {
-                kf[kk] = *reinterpret_cast<const bf16x8*>(K + head + (size_t)kcol * D + 16 * kk + 8 * half);
+                // the scale's sign folded into K, the scores' register operand (see ScoreSign)
+                u32x4 u = *reinterpret_cast<const u32x4*>(K + head + (size_t)kcol * D + 16 * kk + 8 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], s_and, s_xor);
+                kf[kk] = __builtin_bit_cast(bf16x8, u);
                 vf[kk] = *reinterpret_cast<const bf16x8*>(V + head + (size_t)kcol * D + 16 * kk + 8 * half);
             } else {
                 kf[kk] = bf16x8{};
@@ -415,7 +419,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2)))
 void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
             const bf16* __restrict__ dO, const float* __restrict__ Dd, const float* __restrict__ L2,
-            bf16* __restrict__ dQ, int H, int N, int nqb, float c, float scale, const int32_t* __restrict__ kv_limit) {
+            bf16* __restrict__ dQ, int H, int N, int nqb, float c, float scale, uint32_t s_and, uint32_t s_xor,
+            const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[kWaves];
@@ -460,7 +465,11 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         if (qrow < N) {
-            qf[kk] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
+            // the scale's sign folded into Q, the scores' register operand (see ScoreSign)
+            u32x4 u = *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], s_and, s_xor);
+            qf[kk] = __builtin_bit_cast(bf16x8, u);
             gf[kk] = *reinterpret_cast<const bf16x8*>(dO + head + (size_t)qrow * D + 16 * kk + 8 * half);
         } else {
             qf[kk] = bf16x8{};
@@ -592,15 +601,17 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, const bf16* o, co
                        dim3(kRowThreads), 0, stream, o, g, lse, Dd, L2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const float c = scale * kLog2e;
+    // scores use |scale| (or log2(e) at scale 0) with the sign folded into their
+    // register operand; the gradients dQ = scale dS K and dK = scale dS^T Q keep the scale
+    const ScoreSign sg = score_sign(scale, kLog2e, kSignBf16x2);
     const int nkb = (N + kv::kBKV - 1) / kv::kBKV;
     hipLaunchKernelGGL((kv::kernel<D, CAUSAL, MASK>), dim3((unsigned)((long long)B * H * nkb)), dim3(kv::kThreads), 0,
-                       stream, q, k, v, g, Dd, L2, dk, dv, H, N, nkb, c, scale, kv_limit);
+                       stream, q, k, v, g, Dd, L2, dk, dv, H, N, nkb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqb = (N + qd::kBQ - 1) / qd::kBQ;
     hipLaunchKernelGGL((qd::kernel<D, CAUSAL, MASK>), dim3((unsigned)((long long)B * H * nqb)), dim3(qd::kThreads), 0,
-                       stream, q, k, v, g, Dd, L2, dq, H, N, nqb, c, scale, kv_limit);
+                       stream, q, k, v, g, Dd, L2, dq, H, N, nqb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
     return hipGetLastError();
 }
 

@@ -72,6 +72,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// The score sign applied to a 32-bit word of the register-resident score operand
+// (and_mask zeroes it for a zero scale, xor_mask flips sign bits for a negative one).
+__device__ __forceinline__ uint32_t score_signed(uint32_t w, uint32_t and_mask, uint32_t xor_mask) {
+    return (w & and_mask) ^ xor_mask;
+}
+
 // Number of keys row `q` may attend to: keys j < limit are candidates, then the
 // causal condition j <= q is applied on top (limit <= q + 1).
 __device__ __forceinline__ int row_key_limit(int q, int N, bool causal, const int32_t* kv_limit_row) {

@@ -85,7 +85,8 @@ template <int D, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ LSE,
-                int H, int N, int nqb, int items, float c, const int32_t* __restrict__ kv_limit) {
+                int H, int N, int nqb, int items, float c, uint32_t q_and, uint32_t q_xor,
+                const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     constexpr int kBK = T::kBK;
     constexpr int kSub = kBK / 32;  // 32-key slabs per tile
@@ -167,10 +168,15 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         bf16x8 qf[D / 16];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            if (qrow < N)
-                qf[kk] = *reinterpret_cast<const bf16x8*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
-            else
+            if (qrow < N) {
+                // the scale's sign folded into Q (see ScoreSign)
+                u32x4 u = *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], q_and, q_xor);
+                qf[kk] = __builtin_bit_cast(bf16x8, u);
+            } else {
                 qf[kk] = bf16x8{};
+            }
         }
         // after this barrier no wave reads the previous item's stages any more
         __syncthreads();
@@ -321,7 +327,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* lse, int B, int H, int N,
-                  float c, const int32_t* kv_limit, hipStream_t stream) {
+                  ScoreSign sg, const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const long long items = (long long)B * H * nqb;
     // Key limits make block lengths data-dependent: there every block gets its
@@ -330,7 +336,7 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* l
     const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
-                       nqb, (int)items, c, kv_limit);
+                       nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
     return hipGetLastError();
 }
 
@@ -344,10 +350,10 @@ hipError_t launch_fused_bf16(const void* q, const void* k, const void* v, void* 
     const bf16* K = static_cast<const bf16*>(k);
     const bf16* V = static_cast<const bf16*>(v);
     bf16* Ot = static_cast<bf16*>(o);
-    const float c = scale * kLog2e;
+    const ScoreSign sg = score_sign(scale, kLog2e, kSignBf16x2);
     const bool mask = kv_limit != nullptr;
 #define FA_DISPATCH(DD, CC, MM) \
-    if (d == DD && causal == CC && mask == MM) return launch<DD, CC, MM>(Q, K, V, Ot, lse, B, H, N, c, kv_limit, stream);
+    if (d == DD && causal == CC && mask == MM) return launch<DD, CC, MM>(Q, K, V, Ot, lse, B, H, N, sg, kv_limit, stream);
     FA_DISPATCH(64, false, false)
     FA_DISPATCH(64, false, true)
     FA_DISPATCH(64, true, false)

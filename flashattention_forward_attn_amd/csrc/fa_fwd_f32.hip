@@ -35,7 +35,7 @@ template <int D, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                 float* __restrict__ O, float* __restrict__ LSE, int H, int N, int nqb, float c,
-                const int32_t* __restrict__ kv_limit) {
+                uint32_t q_and, uint32_t q_xor, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     __shared__ float Ks[kBK * T::kStride];
     __shared__ float Vs[kBK * T::vStride];
@@ -56,7 +56,11 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
 
     float qf[D / 2];
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) qf[kk] = qrow < N ? Q[head + (size_t)qrow * D + 2 * kk + half] : 0.f;
+    for (int kk = 0; kk < D / 2; ++kk) {
+        // the scale's sign folded into Q (see ScoreSign)
+        const float x = qrow < N ? Q[head + (size_t)qrow * D + 2 * kk + half] : 0.f;
+        qf[kk] = __builtin_bit_cast(float, score_signed(__builtin_bit_cast(uint32_t, x), q_and, q_xor));
+    }
     __syncthreads();
     const int kv_end = max(max(block_max[0], block_max[1]), max(block_max[2], block_max[3]));
     const int ntiles = (kv_end + kBK - 1) / kBK;
@@ -149,11 +153,11 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
 
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
-                  float c, const int32_t* kv_limit, hipStream_t stream) {
+                  ScoreSign sg, const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const dim3 grid((unsigned)((long long)B * H * nqb));
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
-                       nqb, c, kv_limit);
+                       nqb, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
     return hipGetLastError();
 }
 
@@ -163,10 +167,10 @@ hipError_t launch_fused_f32(const float* q, const float* k, const float* v, floa
                             int N, int d, bool causal, float scale, const int32_t* kv_limit,
                             hipStream_t stream) {
     using namespace fused_f32;
-    const float c = scale * kLog2e;
+    const ScoreSign sg = score_sign(scale, kLog2e, kSignF32);
     const bool mask = kv_limit != nullptr;
 #define FA_DISPATCH(DD, CC, MM) \
-    if (d == DD && causal == CC && mask == MM) return launch<DD, CC, MM>(q, k, v, o, lse, B, H, N, c, kv_limit, stream);
+    if (d == DD && causal == CC && mask == MM) return launch<DD, CC, MM>(q, k, v, o, lse, B, H, N, sg, kv_limit, stream);
     FA_DISPATCH(64, false, false)
     FA_DISPATCH(64, false, true)
     FA_DISPATCH(64, true, false)

@@ -166,8 +166,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, const bf16* __restrict__ Qb,
                 const int8_t* __restrict__ signs, const uint8_t* __restrict__ Kc,
                 const int32_t* __restrict__ Ke, const bf16* __restrict__ V, bf16* __restrict__ O,
-                float* __restrict__ LSE, int H, int N, int nqb, int items, float c,
-                const int32_t* __restrict__ kv_limit) {
+                float* __restrict__ LSE, int H, int N, int nqb, int items, float c, uint32_t q_and,
+                uint32_t q_xor, const int32_t* __restrict__ kv_limit) {
     using T = Tile<D>;
     constexpr int kBK = T::kBK, kSub = T::kSub;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
@@ -323,6 +323,12 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
             const int wq = q0 / kQPW + w;
             qscale = 127 + (wq < nqt ? Qe[(size_t)bh * nqt + wq] : 0);
         }
+        // the scale's sign folded into the Q codes (see ScoreSign): E4M3 negates by its
+        // sign bit, and the tile exponent is unchanged
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qf[kk][j] = (int)score_signed((uint32_t)qf[kk][j], q_and, q_xor);
 #pragma unroll
         for (int kk = 0; kk < D / 64; ++kk) launder(qf[kk]);
 
@@ -486,7 +492,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
 
 template <int D, bool CAUSAL, bool MASK, bool QRAW>
 hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const int8_t* signs, const uint8_t* kc,
-                  const int32_t* ke, const bf16* v, bf16* o, float* lse, int B, int H, int N, float c,
+                  const int32_t* ke, const bf16* v, bf16* o, float* lse, int B, int H, int N, ScoreSign sg,
                   const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const long long items = (long long)B * H * nqb;
@@ -494,7 +500,7 @@ hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const in
     const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), dim3(grid), dim3(kThreads), 0, stream, qc, qe, qb, signs,
-                       kc, ke, v, o, lse, H, N, nqb, (int)items, c, kv_limit);
+                       kc, ke, v, o, lse, H, N, nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
     return hipGetLastError();
 }
 
@@ -526,13 +532,14 @@ hipError_t launch_fused_fp8(const uint8_t* qc, const int32_t* qe, const void* q_
     const bf16* Qb = static_cast<const bf16*>(q_bf16);
     const bf16* Vb = static_cast<const bf16*>(v);
     bf16* Ob = static_cast<bf16*>(o);
-    const float c = scale * kLog2e / (float)d;  // the rotation multiplies every score by d
+    // the rotation multiplies every score by d
+    const ScoreSign sg = score_sign(scale, kLog2e / (float)d, kSignE4m3x4);
     const bool mask = kv_limit != nullptr;
     const bool raw = q_bf16 != nullptr;
 #define FA_DISPATCH(DD, CC, MM)                                                                                 \
     if (d == DD && causal == CC && mask == MM)                                                                  \
-        return raw ? launch<DD, CC, MM, true>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream) \
-                   : launch<DD, CC, MM, false>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, c, kv_limit, stream);
+        return raw ? launch<DD, CC, MM, true>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, sg, kv_limit, stream) \
+                   : launch<DD, CC, MM, false>(qc, qe, Qb, signs, kc, ke, Vb, Ob, lse, B, H, N, sg, kv_limit, stream);
     FA_DISPATCH(64, false, false)
     FA_DISPATCH(64, false, true)
     FA_DISPATCH(64, true, false)

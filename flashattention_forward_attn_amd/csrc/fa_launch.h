@@ -10,6 +10,28 @@
 
 namespace fa {
 
+// The sign of the softmax scale, folded into the score operand that a kernel
+// holds in registers.  The kernels' running max, and their masking (a masked
+// score is -inf, and -inf * c must stay -inf), work on c > 0.  A negative scale
+// is computed as the positive one with that operand negated: only sign bits
+// change, the products are exactly negated and so is their sum, so S' c' equals
+// S c bit for bit.  A zero scale is computed with that operand zeroed and
+// c = log2(e): every score is then exactly 0, as scale 0 gives.  and_mask and
+// xor_mask act on each 32-bit word of the operand (sign_bits marks the sign bit
+// of every element packed in a word).
+struct ScoreSign {
+    uint32_t and_mask, xor_mask;
+    float c;  // > 0
+};
+inline ScoreSign score_sign(float scale, float factor, uint32_t sign_bits) {
+    if (scale > 0.f) return ScoreSign{0xffffffffu, 0u, scale * factor};
+    if (scale < 0.f) return ScoreSign{0xffffffffu, sign_bits, -scale * factor};
+    return ScoreSign{0u, 0u, factor};
+}
+constexpr uint32_t kSignBf16x2 = 0x80008000u;
+constexpr uint32_t kSignF32 = 0x80000000u;
+constexpr uint32_t kSignE4m3x4 = 0x80808080u;
+
 // Grid of a forward launch over `blocks` query blocks: with `walk`, one
 // workgroup per CU of the current device (never more than there are blocks),
 // each walking several blocks; otherwise one workgroup per block.  Any grid

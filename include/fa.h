@@ -34,8 +34,11 @@
  * 4 GiB (N*d*2 bytes in bf16, N*d*4 in fp32); and B*H*ceil(N/32) < 2^23 row tiles
  * of 32, i.e. B*H*N < 2^28 rows when N is a multiple of 32 (68 GB per bf16
  * tensor at d = 128).  Offsets are 64-bit, so a tensor may exceed 2^31 elements.
- * The unfused path also needs B*H <= 65535 and N <= 32768.  scale must be finite and
- * positive (the pages use 1/sqrt(d)).
+ * The unfused path also needs B*H <= 65535 and N <= 32768.  scale may be any finite
+ * value: the statement of the problem takes it as a parameter of
+ * softmax(scale * Q K^T + M) V ("谁偷走了 5090 的算力和显存", attention section); the
+ * pages' workloads use 1/sqrt(d).  scale = 0 gives the mean of the valid values and
+ * lse = ln(number of valid keys); a negative scale weights the smallest scores most.
  *
  * Memory and ownership.  Every pointer is device memory owned by the caller.  The
  * library allocates nothing, keeps no pointer after a call returns and has no
@@ -67,7 +70,7 @@ typedef enum {
     FA_ERR_NULL = 1,      /* a required pointer is NULL                              */
     FA_ERR_SHAPE = 2,     /* B, H or N < 1, or sizes beyond the supported shapes     */
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                      */
-    FA_ERR_SCALE = 4,     /* scale is NaN, infinite, zero or negative                */
+    FA_ERR_SCALE = 4,     /* scale is NaN or infinite                                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
     FA_ERR_WORKSPACE = 6, /* unfused, backward or decode path: workspace NULL, too small or misaligned */
     FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch                */

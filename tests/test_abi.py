@@ -68,8 +68,11 @@ def test_fused_validation(lib, name):
     assert fwd(lib, name, d=256) == 3
     assert fwd(lib, name, scale=float("nan")) == 4
     assert fwd(lib, name, scale=float("inf")) == 4
-    assert fwd(lib, name, scale=0.0) == 4
-    assert fwd(lib, name, scale=-0.1) == 4
+    assert fwd(lib, name, scale=float("-inf")) == 4
+    # every finite scale passes (zero and negative too): the next check answers
+    assert fwd(lib, name, scale=0.0, q=Q + 8) == 5
+    assert fwd(lib, name, scale=-0.0, q=Q + 8) == 5
+    assert fwd(lib, name, scale=-0.1, q=Q + 8) == 5
     assert fwd(lib, name, q=Q + 8) == 5
     assert fwd(lib, name, o=O + 2) == 5
     assert fwd(lib, name, l=L + 2) == 5
@@ -93,7 +96,9 @@ def unfused(lib, name="fa_fwd_unfused_bf16", ws=W, ws_bytes=None, B=2, H=3, N=10
 def test_unfused_validation(lib, name):
     assert unfused(lib, name, q=None) == 1
     assert unfused(lib, name, d=80) == 3
-    assert unfused(lib, name, scale=-1.0) == 4
+    assert unfused(lib, name, scale=float("nan")) == 4
+    assert unfused(lib, name, scale=-1.0, ws=None) == 6
+    assert unfused(lib, name, scale=0.0, ws=None) == 6
     assert unfused(lib, name, ws=None) == 6
     assert unfused(lib, name, ws_bytes=100) == 6
     assert unfused(lib, name, ws=W + 128) == 6        # 256-byte alignment
@@ -133,6 +138,8 @@ def test_backward_validation(lib):
     assert bwd(lib, B=1 << 12, H=1 << 12, N=1 << 8, d=64) == 2
     assert bwd(lib, d=32) == 3
     assert bwd(lib, scale=float("nan")) == 4
+    assert bwd(lib, scale=-0.5, q=Q + 8) == 5
+    assert bwd(lib, scale=0.0, q=Q + 8) == 5
     assert bwd(lib, dk=DK + 8) == 5
     assert bwd(lib, g=DO + 4) == 5
     assert bwd(lib, l=L + 1) == 5
@@ -178,7 +185,9 @@ def test_decode_validation(lib):
     assert dec(lib, num_pages=0) == 2
     assert dec(lib, max_pages=65535 * 16 + 1) == 2   # more than 65535 splits
     assert dec(lib, d=96) == 3
-    assert dec(lib, scale=0.0) == 4
+    assert dec(lib, scale=float("nan")) == 4
+    assert dec(lib, scale=0.0, kc=KC + 8) == 5
+    assert dec(lib, scale=-2.0, kc=KC + 8) == 5
     assert dec(lib, kc=KC + 8) == 5
     assert dec(lib, o=OD + 2) == 5
     assert dec(lib, bt=BT + 2) == 5
@@ -225,6 +234,7 @@ def test_fp8_qbf16_validation(lib):
     assert fwd8q(lib, B=1, H=1, N=1 << 24, d=128) == 2      # one head past 4 GiB
     assert fwd8q(lib, d=96) == 3
     assert fwd8q(lib, scale=float("nan")) == 4
+    assert fwd8q(lib, scale=-3.0, q=XQ + 8) == 5
     assert fwd8q(lib, q=XQ + 8) == 5
     assert fwd8q(lib, sg=SG + 8) == 5          # signs are read 16 bytes at a time
     assert fwd8q(lib, kc=CK + 4) == 5
@@ -248,7 +258,9 @@ def test_fp8_validation(lib):
     assert fwd8(lib, qe=None) == 1
     assert fwd8(lib, N=0) == 2
     assert fwd8(lib, d=32) == 3
-    assert fwd8(lib, scale=-1.0) == 4
+    assert fwd8(lib, scale=float("inf")) == 4
+    assert fwd8(lib, scale=-1.0, kc=CK + 4) == 5
+    assert fwd8(lib, scale=0.0, kc=CK + 4) == 5
     assert fwd8(lib, kc=CK + 4) == 5
     assert fwd8(lib, ke=EK + 1) == 5
     assert fwd8(lib, o=VF) == 8               # output over an input
@@ -284,5 +296,5 @@ def test_size_limits(lib):
     assert fwd8(lib, scale=nan, B=1 << 12, H=1 << 11, N=32, d=64) == 2
     assert quant(lib, x=XQ + 2, B=1 << 12, H=1 << 11, N=32, d=64) == 2
     # decode: 256 threads per (sequence, head) in one grid dimension
-    assert dec(lib, scale=0.0, B=65535, H=256) == 4
-    assert dec(lib, scale=0.0, B=65535, H=257) == 2
+    assert dec(lib, scale=nan, B=65535, H=256) == 4
+    assert dec(lib, scale=nan, B=65535, H=257) == 2

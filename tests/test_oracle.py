@@ -5,8 +5,9 @@ Kinds of pin used (every function of the oracle is covered by several):
   - a library routine the definition reduces to (scipy's softmax and logsumexp
     when V is the identity, so O is the attention matrix itself);
   - brute force on tiny inputs in pure Python with math.fsum and no max
-    subtraction;
-  - closed forms (Q = 0, N = 1, the causal first row, constant V, shifted scores);
+    subtraction, at positive, negative and zero scale;
+  - closed forms (Q = 0 or scale = 0, N = 1, the causal first row, constant V,
+    shifted scores);
   - invariants (keys and values permuted together; splitting rows into blocks,
     against the test-side online recurrence in online_reference.py);
   - large-magnitude logits, where a missing max subtraction overflows.
@@ -14,6 +15,7 @@ The last test plants plausible mistakes in a copy of the oracle's source and
 checks that every one of them fails at least one pin.
 """
 import json
+import itertools
 import math
 import os
 
@@ -133,14 +135,13 @@ def pin_brute_force(lib, golden_dir=None):
     for seed, (B, H, N, d) in enumerate([(1, 1, 1, 1), (1, 2, 2, 3), (2, 1, 3, 2), (2, 2, 4, 3)]):
         q, k, v = _rand((B, H, N, d), 10 + seed), _rand((B, H, N, d), 20 + seed), _rand((B, H, N, d), 30 + seed)
         lim = np.random.default_rng(40 + seed).integers(0, N + 1, size=(B, N)).astype(np.int32)
-        for causal in (False, True):
-            for kv in (None, lim):
-                o, lse = oracle.attention(q, k, v, causal=causal, scale=0.8, kv_limit=kv, lib=lib)
-                ro, rl = _brute(q, k, v, causal, 0.8, kv)
-                np.testing.assert_allclose(o, ro, rtol=1e-13, atol=1e-14)
-                fin = np.isfinite(rl)
-                np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-13, atol=1e-14)
-                assert np.array_equal(np.isneginf(lse), ~fin)
+        for causal, kv, scale in itertools.product((False, True), (None, lim), (0.8, -0.8, 0.0)):
+            o, lse = oracle.attention(q, k, v, causal=causal, scale=scale, kv_limit=kv, lib=lib)
+            ro, rl = _brute(q, k, v, causal, scale, kv)
+            np.testing.assert_allclose(o, ro, rtol=1e-13, atol=1e-14)
+            fin = np.isfinite(rl)
+            np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-13, atol=1e-14)
+            assert np.array_equal(np.isneginf(lse), ~fin)
 
 
 def pin_closed_forms(lib, golden_dir=None):
@@ -158,6 +159,11 @@ def pin_closed_forms(lib, golden_dir=None):
             else:
                 np.testing.assert_allclose(o[b, :, i], v[b][:, ok[i]].mean(axis=1), atol=1e-14)
                 np.testing.assert_allclose(lse[b, :, i], math.log(n), atol=1e-14)
+    # scale = 0 (any Q): uniform weights as well
+    o0, l0 = oracle.attention(_rand((B, H, N, d), 58, 5.0), k, v, causal=True, scale=0.0, kv_limit=lim, lib=lib)
+    np.testing.assert_allclose(o0, o, atol=1e-14)
+    np.testing.assert_array_equal(np.isneginf(l0), np.isneginf(lse))
+    np.testing.assert_allclose(l0[np.isfinite(l0)], lse[np.isfinite(lse)], atol=1e-14)
     # N = 1: the only key's value; LSE is its score
     q1, k1, v1 = _rand((1, 3, 1, 5), 52), _rand((1, 3, 1, 5), 53), _rand((1, 3, 1, 5), 54)
     o, lse = oracle.attention(q1, k1, v1, scale=0.5, lib=lib)
@@ -215,10 +221,16 @@ def pin_large_logits(lib, golden_dir=None):
     this goes further, so that a missing max subtraction overflows)."""
     B, H, N, d = 1, 2, 20, 32
     q, k, v = _rand((B, H, N, d), 80, 20.0), _rand((B, H, N, d), 81, 20.0), _rand((B, H, N, d), 82)
-    o, lse = oracle.attention(q, k, v, causal=True, scale=1 / math.sqrt(d), lib=lib)
+    for sc in (1 / math.sqrt(d), -1 / math.sqrt(d)):
+        _large_logits_case(lib, q, k, v, sc)
+
+
+def _large_logits_case(lib, q, k, v, sc):
+    B, H, N, d = q.shape
+    o, lse = oracle.attention(q, k, v, causal=True, scale=sc, lib=lib)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     for h in range(H):
-        s = (q[0, h] @ k[0, h].T) / math.sqrt(d)
+        s = (q[0, h] @ k[0, h].T) * sc
         assert s.max() > 710
         for i in range(N):
             row = s[i, :i + 1]
