@@ -35,6 +35,15 @@ Besides the headline number the line carries:
                   1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TFLOP/s.
 
 --path backward / --path decode / --path fp8 make that pass the timed step instead.
+
+Order: the headline's inputs go to the device first, then the other legs run
+back to back on the GPU, then the headline's warm-up and timed steps, and only
+then the oracle baselines (host work).  So the timed steps start on a GPU that
+has been busy: an idle GPU drops its clock, and raising it again takes longer
+than a few warm-up launches (tens of milliseconds).  After the
+timed steps the shader clock is sampled with rocm-smi while the same kernel
+keeps running, and roofline.frac_at_measured_clock rates the kernel against the
+MFMA peak scaled to that clock.
 """
 from __future__ import annotations
 
@@ -48,6 +57,7 @@ import numpy as np
 
 HEADLINE = "bf16_causal_b2h32n4096d128"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_SCLK_MHZ = 2400.0  # the clock the published peaks assume
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
 BWD_METRIC = "attention bwd TFLOP/s (bf16, nominal 10*N^2*d per head) and % of MI355X MFMA peak"
 DEC_METRIC = "paged decode attention GB/s (bf16, keys and values read once) and % of MI355X HBM bandwidth"
@@ -69,15 +79,33 @@ KERNEL_SOURCES = {
 }
 
 
-def host_threads() -> int:
+# The GPU machines allot 16 host CPUs to a job that drives one GPU, whatever the
+# node shows; the oracle runs on that share.
+HOST_SHARE = 16
+
+
+def host_cpus() -> int:
+    """CPUs this process may run on (what nproc reports)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def host_threads() -> int:
+    return max(1, min(HOST_SHARE, host_cpus()))
 
 
 def host_cpu_model() -> str:
+    """lscpu's model name (from /proc/cpuinfo if lscpu is missing)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -86,6 +114,49 @@ def host_cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def host_fields(threads: int) -> dict:
+    return {"cores": threads, "host_cpus": host_cpus(), "cpu_model": host_cpu_model(),
+            "threads_note": f"the oracle runs on {threads} threads: the job's share of the host "
+                            f"({HOST_SHARE} CPUs per GPU job), of {host_cpus()} CPUs the node shows"}
+
+
+def sample_sclk(torch, launch, seconds: float = 1.0):
+    """Median shader clock (MHz, rocm-smi) while `launch` runs back to back for about
+    `seconds`; None if rocm-smi is unavailable."""
+    import re
+    import subprocess
+    import threading
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                     timeout=5).stdout
+                m = re.search(r'"sclk clock speed:": "\((\d+)Mhz\)"', out)
+                if m:
+                    samples.append(int(m.group(1)))
+            except (OSError, subprocess.SubprocessError):
+                return
+            time.sleep(0.02)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=10)
+    if not samples:
+        return None
+    samples.sort()
+    return {"sclk_mhz_median": samples[len(samples) // 2], "sclk_mhz_min": samples[0], "sclk_mhz_max": samples[-1],
+            "samples": len(samples), "how": f"rocm-smi --showclocks while the timed kernel runs back to back "
+                                             f"for {seconds:.1f} s after the timed steps"}
 
 
 def device_inputs(torch, x):
@@ -99,6 +170,9 @@ def device_inputs(torch, x):
     return q, k, v, lim
 
 
+LAST_HOST_US = [0.0]  # host time per call of the last timed loop (microseconds)
+
+
 def time_launches(torch, launch, steps: int, warmup: int) -> float:
     """Mean milliseconds per launch, HIP events on the current (launch) stream."""
     for _ in range(warmup):
@@ -107,10 +181,12 @@ def time_launches(torch, launch, steps: int, warmup: int) -> float:
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
         launch()
     end.record(stream)
+    LAST_HOST_US[0] = (time.perf_counter() - t0) / steps * 1e6
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
@@ -131,8 +207,9 @@ def launch_spread(torch, launch, n: int) -> dict:
             "min_ms": round(t[0], 5)}
 
 
-def measure_fused(torch, binding, x, steps, warmup, spread=0):
-    """Mean ms per fused launch; with spread > 0 also launch_spread over that many launches."""
+def fused_launcher(torch, binding, x):
+    """Device copies of x's inputs and outputs, and a function launching the fused
+    forward on them (one step)."""
     w = x.workload
     q, k, v, lim = device_inputs(torch, x)
     o = torch.empty_like(q)
@@ -143,9 +220,18 @@ def measure_fused(torch, binding, x, steps, warmup, spread=0):
     def launch():
         fn(q, k, v, o, lse, w.causal, w.scale, lim, stream)
 
+    return launch
+
+
+def measure_fused(torch, binding, x, steps, warmup, spread=0, clock=False, launch=None):
+    """Mean ms per fused launch; with spread > 0 also launch_spread over that many
+    launches (and with clock the shader clock sampled while the kernel runs on)."""
+    launch = launch or fused_launcher(torch, binding, x)
     ms = time_launches(torch, launch, steps, warmup)
     sp = launch_spread(torch, launch, spread) if spread else None
-    del q, k, v, o, lse, lim
+    clk = sample_sclk(torch, launch) if clock else None
+    if clock:
+        return ms, sp, clk
     return (ms, sp) if spread else ms
 
 
@@ -235,7 +321,7 @@ def cpu_baseline_decode(xd):
     t0 = time.perf_counter()
     oracle.decode_paged(q, kc, vc, xd.block_table, xd.seq_lens, xd.workload.scale, nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
+    return {"value": decode_bytes(xd) / dt / 1e9, "unit": "GB/s", **host_fields(threads), "kind": "oracle",
             "sample": f"the whole {xd.workload.name} workload, fp64, {dt:.3f} s; same algorithmic bytes",
             "seconds": round(dt, 3)}
 
@@ -314,7 +400,7 @@ def cpu_baseline_fp8(x, target_seconds: float):
             break
         nh *= 2
     flops = w.flops() / (w.B * w.H) * nh
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **host_fields(threads), "kind": "oracle",
             "sample": f"heads 0..{nh - 1} of batch item 0 of {w.name}: quantisation and attention on the codes, "
                       f"fp64, {dt:.1f} s", "seconds": round(dt, 3)}
 
@@ -373,8 +459,8 @@ def cpu_baseline(x, target_seconds: float):
     return {
         "value": ids.size * flops_per_row / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle", "cpu_model": host_cpu_model(),
+        **host_fields(threads),
+        "kind": "oracle",
         "sample": f"{ids.size} of {rows_total} query rows of {w.name}, evenly spaced, fp64, "
                   f"{dt:.1f} s; FLOPs per row = workload FLOPs / rows",
         "seconds": round(dt, 3),
@@ -398,8 +484,8 @@ def cpu_baseline_backward(x, g):
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": nh,
-        "kind": "oracle", "cpu_model": host_cpu_model(),
+        **host_fields(threads),
+        "kind": "oracle",
         "sample": f"full backward of heads 0..{nh - 1} of batch item 0 of {w.name}, fp64, {dt:.1f} s; "
                   f"nominal backward FLOPs of those heads",
         "seconds": round(dt, 3),
@@ -415,6 +501,52 @@ def load_traffic(path_file: str, path: str, workload: str):
     if t and t.get("kernel_source_sha256") == _kernel_digest(path):
         return t.get("bytes_per_launch")
     return None
+
+
+def measure_extras(torch, binding, inputs, x, g, w, args):
+    """The unfused baseline, the other bf16 workloads, the backward, the FP8 forward
+    and the paged decode, each timed the same way, back to back on the GPU.  Their
+    oracle baselines (host work) are returned as deferred jobs, run after the
+    headline's timed steps."""
+    out, deferred = {}, []
+    ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
+    ugbs = unfused_bytes(w) / (ums * 1e-3) / 1e9
+    out["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
+                      "GB/s": round(ugbs, 1), "hbm_frac": round(ugbs / PEAK_HBM_GBS, 4),
+                      "traffic": load_traffic(args.traffic, "unfused", w.name)}
+    others = {}
+    for name, ow in inputs.WORKLOADS.items():
+        if name == w.name or ow.dtype != "bf16":
+            continue
+        ox = inputs.generate(ow)
+        oms = measure_fused(torch, binding, ox, args.steps, args.warmup)
+        entry = {"ms": round(oms, 5), "TFLOP/s": round(ow.flops() / (oms * 1e-3) / 1e12, 2),
+                 "frac": round(ow.flops() / (oms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "traffic": load_traffic(args.traffic, "fused", name)}
+        if ox.kv_limit is not None:
+            entry["effective_TFLOP/s"] = round(effective_flops(ox) / (oms * 1e-3) / 1e12, 2)
+        others[name] = entry
+        del ox
+    out["workloads"] = others
+    if g is not None:
+        bms = measure_backward(torch, binding, x, g, max(20, args.steps // 2), max(10, args.warmup // 4))
+        btf = w.bwd_flops() / (bms * 1e-3) / 1e12
+        out["backward"] = {
+            "metric": BWD_METRIC, "value": round(btf, 2), "unit": "TFLOP/s", "ms_per_step": round(bms, 5),
+            "flops_per_step": w.bwd_flops(),
+            "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic(args.traffic, "backward", w.name), "note": BWD_NOTE},
+        }
+        out["fp8"] = fp8_entry(torch, binding, x, args.steps, args.warmup, args.traffic, False, args.cpu_seconds)
+        xd = inputs.generate_decode(inputs.DECODE_WORKLOADS[args.decode_workload])
+        out["decode"] = decode_entry(torch, binding, xd, max(20, args.steps // 2), max(10, args.warmup // 4),
+                                     args.traffic, False)
+        if not args.no_cpu_baseline:
+            deferred.append(lambda: out["backward"].__setitem__("cpu_baseline", cpu_baseline_backward(x, g)))
+            deferred.append(lambda: out["fp8"].__setitem__("cpu_baseline", cpu_baseline_fp8(x, args.cpu_seconds)))
+            deferred.append(lambda: out["decode"].__setitem__("cpu_baseline", cpu_baseline_decode(xd)))
+    return out, deferred
 
 
 def main() -> int:
@@ -501,16 +633,28 @@ def main() -> int:
         return 2
     x = inputs.generate(w)
     g = inputs.grad_output(w) if w.dtype == "bf16" else None
+    # The other legs run first: the headline's warm-up and timed steps then start
+    # on a GPU that has been busy, as a kernel inside a model step would.
+    extras, deferred = {}, []
+    launch = fused_launcher(torch, binding, x) if args.path == "fused" else None
+    if not args.no_extras and args.path == "fused":
+        extras, deferred = measure_extras(torch, binding, inputs, x, g, w, args)
     spread = None
+    clock = None
     if args.path == "backward":
         ms, spread = measure_backward(torch, binding, x, g, args.steps, args.warmup, spread=SPREAD_LAUNCHES)
         tflops = w.bwd_flops() / (ms * 1e-3) / 1e12
     elif args.path == "fused":
-        ms, spread = measure_fused(torch, binding, x, args.steps, args.warmup, spread=SPREAD_LAUNCHES)
+        ms, spread, clock = measure_fused(torch, binding, x, args.steps, args.warmup, spread=SPREAD_LAUNCHES,
+                                          clock=True, launch=launch)
+        host_us = LAST_HOST_US[0]
         tflops = w.flops() / (ms * 1e-3) / 1e12
     else:
         ms = measure_unfused(torch, binding, x, args.steps, args.warmup)
         tflops = w.flops() / (ms * 1e-3) / 1e12
+    # host work only after every timed GPU leg
+    for job in deferred:
+        job()
     traffic = load_traffic(args.traffic, args.path, w.name)
 
     line = {
@@ -533,11 +677,18 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if clock is not None:
+        # the same fraction against the MFMA peak at the clock the GPU ran at
+        line["roofline"]["clock"] = clock
+        line["roofline"]["frac_at_measured_clock"] = round(
+            tflops / (PEAK_BF16_TFLOPS * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ), 4)
     if spread is not None:
         fl = w.bwd_flops() if args.path == "backward" else w.flops()
         spread["TFLOP/s_at_median"] = round(fl / (spread["median_ms"] * 1e-3) / 1e12, 2)
         spread["TFLOP/s_at_min"] = round(fl / (spread["min_ms"] * 1e-3) / 1e12, 2)
         line["per_launch"] = spread
+    if args.path == "fused":
+        line["host_us_per_call"] = round(host_us, 1)
     if args.path == "unfused":
         ub = unfused_bytes(w)
         gbs = ub / (ms * 1e-3) / 1e9
@@ -549,44 +700,10 @@ def main() -> int:
         line["config"]["bytes_per_step"] = ub
     if args.path == "backward":
         line["roofline"]["note"] = BWD_NOTE
-    if not args.no_extras and args.path == "fused":
-        ums = measure_unfused(torch, binding, x, max(5, args.steps // 5), 3)
-        ugbs = unfused_bytes(w) / (ums * 1e-3) / 1e9
-        line["unfused"] = {"ms_per_step": round(ums, 4), "TFLOP/s": round(w.flops() / (ums * 1e-3) / 1e12, 2),
-                           "GB/s": round(ugbs, 1), "hbm_frac": round(ugbs / PEAK_HBM_GBS, 4),
-                           "traffic": load_traffic(args.traffic, "unfused", w.name),
-                           "fused_speedup": round(ums / ms, 2)}
-        others = {}
-        for name, ow in inputs.WORKLOADS.items():
-            if name == w.name or ow.dtype != "bf16":
-                continue
-            ox = inputs.generate(ow)
-            oms = measure_fused(torch, binding, ox, args.steps, args.warmup)
-            entry = {"ms": round(oms, 5), "TFLOP/s": round(ow.flops() / (oms * 1e-3) / 1e12, 2),
-                     "frac": round(ow.flops() / (oms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            if ox.kv_limit is not None:
-                entry["effective_TFLOP/s"] = round(effective_flops(ox) / (oms * 1e-3) / 1e12, 2)
-            others[name] = entry
-            del ox
-        line["workloads"] = others
-    if not args.no_extras and args.path == "fused" and g is not None:
-        bms = measure_backward(torch, binding, x, g, max(20, args.steps // 2), max(10, args.warmup // 4))
-        btf = w.bwd_flops() / (bms * 1e-3) / 1e12
-        line["backward"] = {
-            "metric": BWD_METRIC, "value": round(btf, 2), "unit": "TFLOP/s", "ms_per_step": round(bms, 5),
-            "flops_per_step": w.bwd_flops(),
-            "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": load_traffic(args.traffic, "backward", w.name), "note": BWD_NOTE},
-        }
-        if not args.no_cpu_baseline:
-            line["backward"]["cpu_baseline"] = cpu_baseline_backward(x, g)
-        line["fp8"] = fp8_entry(torch, binding, x, args.steps, args.warmup, args.traffic, not args.no_cpu_baseline,
-                                args.cpu_seconds)
-        xd = inputs.generate_decode(inputs.DECODE_WORKLOADS[args.decode_workload])
-        line["decode"] = decode_entry(torch, binding, xd, max(20, args.steps // 2), max(10, args.warmup // 4),
-                                      args.traffic, not args.no_cpu_baseline)
-        del xd
+    if extras:
+        if "unfused" in extras:
+            extras["unfused"]["fused_speedup"] = round(extras["unfused"]["ms_per_step"] / ms, 2)
+        line.update(extras)
     if not args.no_cpu_baseline:
         if args.path == "backward":
             line["cpu_baseline"] = cpu_baseline_backward(x, g)
