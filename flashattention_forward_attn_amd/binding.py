@@ -45,6 +45,12 @@ def open_library(path: str):
     C signatures declared.  Raises if the file is missing."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m flashattention_forward_attn_amd.build`")
+    # torch first: the library must bind to the HIP runtime torch loads, since
+    # the tensors, streams and device context it is handed are that runtime's.
+    # torch's HIP library asks for its bundled runtime by file name, so a library
+    # loaded before torch would bring in the system runtime and torch would then
+    # load a second one beside it.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     fwd = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]

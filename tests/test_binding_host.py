@@ -102,3 +102,26 @@ def test_fp8_qbf16_checks():
         binding.fa_fwd_fp8_qbf16(q, signs, kc, torch.zeros(B, H, 2, dtype=torch.int32), q, *out, False, 0.125)
     with pytest.raises(ValueError, match="q must be a GPU tensor"):
         binding.fa_fwd_fp8_qbf16(q, signs, kc, ke, q, *out, False, 0.125)
+
+
+def test_one_hip_runtime_whatever_loads_first():
+    """A fresh process that calls into the library before importing torch maps one
+    HIP runtime, the one torch uses: the binding imports torch before it opens the
+    library.  (torch's HIP library asks for its bundled runtime by file name, so the
+    other order would map the system runtime and then torch's beside it.)"""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "from flashattention_forward_attn_amd import binding\n"
+        "binding.fa_decode_workspace_bytes(1, 1, 128, 1)\n"
+        "import torch\n"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(paths), *sorted(paths))\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    count, *paths = out.stdout.split()
+    assert int(count) == 1, paths
+    assert os.path.dirname(paths[0]) == os.path.join(os.path.dirname(torch.__file__), "lib"), paths
