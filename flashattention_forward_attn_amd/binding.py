@@ -21,7 +21,10 @@ SINGLE_STAGE_LIBRARY = os.path.join(HERE, "libfa_single_stage.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
-                5: "FA_ERR_ALIGN", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIAS"}
+                5: "FA_ERR_ALIGN", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIAS",
+                9: "FA_ERR_SCRATCH"}
+# bytes of the no-allocation decode's static buffer (FA_DECODE_SCRATCH_BYTES)
+FA_DECODE_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -70,6 +73,8 @@ def open_library(path: str):
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_paged_bf16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_decode_paged_bf16.restype = ctypes.c_int
+    lib.fa_decode_paged_bf16_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_decode_paged_bf16_noalloc.restype = ctypes.c_int
     lib.fa_fp8_quantize_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_fp8_quantize_bf16.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp]
@@ -247,11 +252,9 @@ def fa_decode_workspace_bytes(B: int, H: int, d: int, max_pages: int) -> int:
     return int(load().fa_decode_workspace_bytes(B, H, d, max_pages))
 
 
-def fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: float, workspace=None,
-                         stream=None) -> None:
-    """Decode over a paged cache: q, o bf16 [B, H, d]; k_cache, v_cache bf16 [num_pages, H, 16, d];
-    block_table int32 [B, max_pages]; seq_lens int32 [B]; lse fp32 [B, H]; workspace a device uint8
-    tensor of at least fa_decode_workspace_bytes(B, H, d, max_pages) bytes."""
+def _decode_shapes(q, k_cache, v_cache, block_table, seq_lens, o, lse):
+    """(B, H, d, page_size, max_pages, num_pages) of a paged decode call, after
+    checking every tensor's dtype, shape and layout."""
     import torch
     if not all(hasattr(t, "dim") for t in (q, k_cache, block_table)) or q.dim() != 3 or k_cache.dim() != 4 \
             or block_table.dim() != 2:
@@ -266,12 +269,32 @@ def fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, sca
     _expect(seq_lens, "seq_lens", torch.int32, (B,))
     _expect(o, "o", torch.bfloat16, (B, H, d))
     _expect(lse, "lse", torch.float32, (B, H))
+    return B, H, d, page_size, max_pages, num_pages
+
+
+def fa_decode_paged_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: float, workspace=None,
+                         stream=None) -> None:
+    """Decode over a paged cache: q, o bf16 [B, H, d]; k_cache, v_cache bf16 [num_pages, H, 16, d];
+    block_table int32 [B, max_pages]; seq_lens int32 [B]; lse fp32 [B, H]; workspace a device uint8
+    tensor of at least fa_decode_workspace_bytes(B, H, d, max_pages) bytes."""
+    B, H, d, page_size, max_pages, num_pages = _decode_shapes(q, k_cache, v_cache, block_table, seq_lens, o, lse)
     nbytes = _workspace(workspace)
     _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, o=o, lse=lse,
                 workspace=workspace)
     _check(load().fa_decode_paged_bf16(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
                                        _ptr(o), _ptr(lse), B, H, d, page_size, max_pages, num_pages, float(scale),
                                        _ptr(workspace), nbytes, _stream(stream)))
+
+
+def fa_decode_paged_bf16_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, scale: float,
+                                 stream=None) -> None:
+    """fa_decode_paged_bf16 without a workspace: the library's static per-GPU buffer
+    of FA_DECODE_SCRATCH_BYTES holds the partials.  Same tensors as fa_decode_paged_bf16."""
+    B, H, d, page_size, max_pages, num_pages = _decode_shapes(q, k_cache, v_cache, block_table, seq_lens, o, lse)
+    _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, seq_lens=seq_lens, o=o, lse=lse)
+    _check(load().fa_decode_paged_bf16_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                               _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, d, page_size, max_pages,
+                                               num_pages, float(scale), _stream(stream)))
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[float] = None, stream=None):

@@ -1,6 +1,7 @@
 // fa_api.cpp -- the C ABI declared in include/fa.h: argument validation on the
 // host, then dispatch to the HIP launchers.  No allocation, no synchronisation,
-// no global state, no exception crosses the boundary.
+// no exception crosses the boundary; the only global state is the decode path's
+// static scratch buffer and its per-device address.
 #include "fa.h"
 
 #include <math.h>
@@ -26,6 +27,7 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 constexpr size_t kWsAlign = 256;
+static_assert((int64_t)FA_DECODE_SCRATCH_BYTES == fa::kDecodeScratchBytes, "one scratch size");
 constexpr int kUnfusedMaxN = 32768;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -115,6 +117,43 @@ size_t decode_workspace_bytes(int B, int H, int d, int max_pages) {
     return (size_t)fa::decode_workspace_floats(B, H, d, max_pages) * 4;
 }
 
+// Checks shared by the decode entry points, in order: pointers, sizes, head
+// dimension, scale, alignment.
+fa_status decode_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, const void* o, const float* lse, int B, int H, int d, int page_size,
+                      int max_pages, int num_pages, float scale) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage ||
+        fa::decode_max_splits(max_pages) > 65535 ||
+        (int64_t)B * H * 256 > (int64_t)UINT32_MAX)  // 256 threads per (sequence, head) in each launch
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+// o, lse and the workspace (if any) overlap no input and no other output.
+fa_status decode_alias(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, const void* o, const float* lse, int B, int H, int d, int max_pages,
+                       int num_pages, const void* workspace, size_t workspace_bytes) {
+    const int64_t row_bytes = (int64_t)B * H * d * 2;
+    const int64_t cache_bytes = (int64_t)num_pages * H * fa::kDecodePage * d * 2;
+    const Range ins[] = {span(q, row_bytes), span(k_cache, cache_bytes), span(v_cache, cache_bytes),
+                         span(block_table, (int64_t)B * max_pages * 4), span(seq_lens, (int64_t)B * 4)};
+    const Range outs[] = {span(o, row_bytes), span(lse, (int64_t)B * H * 4),
+                          span(workspace, workspace ? (int64_t)workspace_bytes : 0)};
+    for (int i = 0; i < 3; ++i) {
+        for (Range in : ins)
+            if (overlap(outs[i], in)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+    }
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,32 +233,35 @@ fa_status fa_decode_paged_bf16(const fa_bf16* q, const fa_bf16* k_cache, const f
                                const int32_t* block_table, const int32_t* seq_lens, fa_bf16* o, float* lse, int B,
                                int H, int d, int page_size, int max_pages, int num_pages, float scale,
                                void* workspace, size_t workspace_bytes_given, void* stream) {
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
-    if (B < 1 || H < 1 || B > 65535 || H > 65535 || max_pages < 1 || num_pages < 1 || page_size != fa::kDecodePage ||
-        fa::decode_max_splits(max_pages) > 65535 ||
-        (int64_t)B * H * 256 > (int64_t)UINT32_MAX)  // 256 threads per (sequence, head) in each launch
-        return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-    if (!isfinite(scale)) return FA_ERR_SCALE;
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
-        return FA_ERR_ALIGN;
+    fa_status st = decode_args(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, page_size, max_pages,
+                               num_pages, scale);
+    if (st != FA_OK) return st;
     const size_t need = decode_workspace_bytes(B, H, d, max_pages);
     if (!workspace || workspace_bytes_given < need || !aligned(workspace, kWsAlign)) return FA_ERR_WORKSPACE;
-    const int64_t row_bytes = (int64_t)B * H * d * 2;
-    const int64_t cache_bytes = (int64_t)num_pages * H * fa::kDecodePage * d * 2;
-    const Range ins[] = {span(q, row_bytes), span(k_cache, cache_bytes), span(v_cache, cache_bytes),
-                         span(block_table, (int64_t)B * max_pages * 4), span(seq_lens, (int64_t)B * 4)};
-    const Range outs[] = {span(o, row_bytes), span(lse, (int64_t)B * H * 4), span(workspace, (int64_t)need)};
-    for (int i = 0; i < 3; ++i) {
-        for (Range in : ins)
-            if (overlap(outs[i], in)) return FA_ERR_ALIAS;
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
-    }
+    st = decode_alias(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, max_pages, num_pages, workspace,
+                      need);
+    if (st != FA_OK) return st;
     return hip_status(fa::launch_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, max_pages,
                                              num_pages, scale, static_cast<float*>(workspace),
                                              static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_decode_paged_bf16_noalloc(const fa_bf16* q, const fa_bf16* k_cache, const fa_bf16* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens, fa_bf16* o, float* lse,
+                                       int B, int H, int d, int page_size, int max_pages, int num_pages,
+                                       float scale, void* stream) {
+    fa_status st = decode_args(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, page_size, max_pages,
+                               num_pages, scale);
+    if (st != FA_OK) return st;
+    if ((int64_t)decode_workspace_bytes(B, H, d, max_pages) > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+    // the static buffer is the library's own: it cannot overlap the caller's memory
+    st = decode_alias(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, max_pages, num_pages, nullptr, 0);
+    if (st != FA_OK) return st;
+    float* scratch = nullptr;
+    const hipError_t e = fa::decode_scratch(&scratch);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    return hip_status(fa::launch_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H, d, max_pages,
+                                             num_pages, scale, scratch, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_fp8_quantize_bf16(const fa_bf16* x, const int8_t* signs, uint8_t* codes, int32_t* exps, int B, int H,
@@ -297,8 +339,9 @@ const char* fa_status_str(fa_status s) {
         case FA_ERR_SCALE: return "scale must be finite";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse and kv_limit 4-byte aligned";
         case FA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
-        case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch or a lookup";
         case FA_ERR_ALIAS: return "an output overlaps an input, the other output or the workspace";
+        case FA_ERR_SCRATCH: return "the call needs more scratch memory than the library's static buffer holds";
     }
     return "unknown status";
 }

@@ -26,6 +26,8 @@
 //      split.
 //   2. combine: one workgroup per (sequence, head) merges its splits:
 //      m = max m_s, l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -263,6 +265,34 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 }
 
 }  // namespace decode
+
+// Workspace of the no-allocation entry point: one copy per GPU, created with the
+// code object and held until the process ends.  In host code its name stands for
+// a host-side shadow, never a device address: every use goes through the address
+// decode_scratch looks up.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / 4];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex scratch_mutex;
+float* scratch_ptr[kScratchDevices] = {};  // device address per device, once looked up
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                               const int32_t* seq_lens, void* o, float* lse, int B, int H, int d, int max_pages,

@@ -81,6 +81,10 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
                               const int32_t* seq_lens, void* o, float* lse, int B, int H, int d, int max_pages,
                               int num_pages, float scale, float* workspace, hipStream_t stream);
 
+// Device address of the decode path's static scratch buffer (kDecodeScratchBytes)
+// on the current device; looked up once per device, on its first use.
+hipError_t decode_scratch(float** ptr);
+
 // Rotate (random signs, Hadamard) and encode rows of a bf16 [B, H, N, d] tensor
 // to E4M3 codes [B, H, N, d] with per-tile exponents.
 hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* codes, int32_t* exps, int B, int H, int N,

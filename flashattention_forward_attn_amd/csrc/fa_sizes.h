@@ -23,6 +23,10 @@ inline int64_t decode_workspace_floats(int B, int H, int d, int max_pages) {
     return decode_part_o_floats(B, H, d, max_pages) + ((int64_t)B * H * decode_max_splits(max_pages) * 2 + 63) / 64 * 64;
 }
 
+// The no-allocation decode entry point keeps its splits' partials in a static
+// device buffer of this many bytes per GPU instead of a caller's workspace.
+constexpr int64_t kDecodeScratchBytes = (int64_t)16 << 20;
+
 // FP8 forward: Q codes come in tiles of kFp8QTile rows, K codes in tiles of
 // kFp8KTile rows, one int32 exponent per tile ([B, H, ceil(N / tile)]).
 constexpr int kFp8QTile = 32;

@@ -73,8 +73,10 @@ typedef enum {
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse / kv_limit not 4-byte aligned */
     FA_ERR_WORKSPACE = 6, /* unfused, backward or decode path: workspace NULL, too small or misaligned */
-    FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch                */
-    FA_ERR_ALIAS = 8      /* an output overlaps an input, the other output or the workspace */
+    FA_ERR_HIP = 7,       /* the HIP runtime rejected a kernel launch or a lookup    */
+    FA_ERR_ALIAS = 8,     /* an output overlaps an input, the other output or the workspace */
+    FA_ERR_SCRATCH = 9    /* fa_decode_paged_bf16_noalloc: the call needs more than
+                             FA_DECODE_SCRATCH_BYTES of scratch */
 } fa_status;
 
 /*
@@ -225,6 +227,39 @@ fa_status fa_decode_paged_bf16(const fa_bf16 *q, const fa_bf16 *k_cache, const f
                                fa_bf16 *o, float *lse,
                                int B, int H, int d, int page_size, int max_pages, int num_pages,
                                float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of the static device buffer fa_decode_paged_bf16_noalloc uses in place of
+ * a workspace, on each GPU the library runs on.
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * fa_decode_paged_bf16 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as fa_decode_paged_bf16 without the workspace, and
+ * the same kernels: the splits' partials go to a buffer of FA_DECODE_SCRATCH_BYTES
+ * that the library holds in static device memory, one copy per GPU, until the
+ * process ends.  The call allocates nothing.
+ *
+ * Limit: fa_decode_workspace_bytes(B, H, d, max_pages) <= FA_DECODE_SCRATCH_BYTES,
+ * else FA_ERR_SCRATCH (checked on the host before anything is launched).  With
+ * n = B * H * ceil(max_pages / 16) splits (d floats and a (max, sum) pair each)
+ * that is n <= 32263 for d = 128 and n <= 63550 for d = 64; B = 64, H = 32,
+ * max_pages = 128, d = 128 (n = 16384) fits.
+ *
+ * Every call on one GPU shares that GPU's buffer, and the buffer keeps the last
+ * call's contents; nothing in it has to start at zero, since a call reads only
+ * what its own first kernel wrote.  Calls on one stream are ordered; calls that
+ * may overlap on one GPU (different streams, or host threads without ordering)
+ * race on the buffer and must not be made.  The first call on a device looks up
+ * the buffer's device address there (FA_ERR_HIP if that fails).
+ */
+fa_status fa_decode_paged_bf16_noalloc(const fa_bf16 *q, const fa_bf16 *k_cache, const fa_bf16 *v_cache,
+                                       const int32_t *block_table, const int32_t *seq_lens,
+                                       fa_bf16 *o, float *lse,
+                                       int B, int H, int d, int page_size, int max_pages, int num_pages,
+                                       float scale, void *stream);
 
 /*
  * FP8 forward, step 1: rotate and encode one of Q or K.  Every row x (length d)

@@ -47,7 +47,7 @@ def test_single_stage_build_exports_the_same_functions():
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_str(99).decode() == "unknown status"
@@ -198,6 +198,44 @@ def test_decode_validation(lib):
     assert dec(lib, l=BT) == 8                 # lse over the block table
     assert dec(lib, ws=OD) == 8                # workspace over the output
     assert dec(lib, l=OD + 16) == 8            # lse over the output
+
+
+def decn(lib, q=QD, kc=KC, vc=VC, bt=BT, sl=SL, o=OD, l=LD, B=2, H=3, d=128, page=16, max_pages=8, num_pages=20,
+         scale=0.125):
+    return lib.fa_decode_paged_bf16_noalloc(q, kc, vc, bt, sl, o, l, B, H, d, page, max_pages, num_pages, scale, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks what fa_decode_paged_bf16 checks, in the same
+    order, then the scratch limit; every case here fails before anything runs."""
+    nan = float("nan")
+    assert decn(lib, q=None) == 1
+    assert decn(lib, l=None) == 1
+    assert decn(lib, B=0) == 2
+    assert decn(lib, page=32) == 2
+    assert decn(lib, max_pages=65535 * 16 + 1) == 2
+    assert decn(lib, d=96) == 3
+    assert decn(lib, scale=nan) == 4
+    assert decn(lib, scale=0.0, kc=KC + 8) == 5
+    assert decn(lib, o=OD + 2) == 5
+    assert decn(lib, o=KC + 4096) == 8
+    assert decn(lib, l=OD + 16) == 8
+    # scratch: n = B * H * ceil(max_pages / 16) splits of d floats and a (max, sum)
+    # pair, each part padded to 64 floats, within FA_DECODE_SCRATCH_BYTES
+    cap = binding.FA_DECODE_SCRATCH_BYTES
+    assert lib.fa_decode_workspace_bytes(1, 32263, 128, 16) <= cap < lib.fa_decode_workspace_bytes(1, 32264, 128, 16)
+    assert lib.fa_decode_workspace_bytes(1, 63550, 64, 16) <= cap < lib.fa_decode_workspace_bytes(1, 63551, 64, 16)
+    assert decn(lib, B=1, H=32264, max_pages=16, o=OD + 2) == 5       # sizes pass, alignment fails next
+    assert decn(lib, B=1, H=32264, max_pages=16) == 9
+    assert decn(lib, B=64, H=32, max_pages=257) == 9                    # 17 splits of 128 floats
+    assert decn(lib, B=1, H=63551, d=64, max_pages=16) == 9
+    assert decn(lib, B=1, H=32263, max_pages=16, o=OD + 2) == 5         # within the limit: next check fails
+
+
+def test_decode_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.FA_DECODE_SCRATCH_BYTES
 
 
 def test_decode_workspace_bytes(lib):
