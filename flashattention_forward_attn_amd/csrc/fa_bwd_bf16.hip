@@ -597,22 +597,19 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, const bf16* o, co
                   bf16* dq, bf16* dk, bf16* dv, int B, int H, int N, float scale, const int32_t* kv_limit,
                   float* Dd, float* L2, hipStream_t stream) {
     const long long rows = (long long)B * H * N;
-    hipLaunchKernelGGL((rows_kernel<D>), dim3((unsigned)((rows * 16 + kRowThreads - 1) / kRowThreads)),
-                       dim3(kRowThreads), 0, stream, o, g, lse, Dd, L2, rows);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(rows_kernel<D>, dim3((unsigned)((rows * 16 + kRowThreads - 1) / kRowThreads)),
+                                 dim3(kRowThreads), 0, stream, o, g, lse, Dd, L2, rows);
     if (e != hipSuccess) return e;
     // scores use |scale| (or log2(e) at scale 0) with the sign folded into their
     // register operand; the gradients dQ = scale dS K and dK = scale dS^T Q keep the scale
     const ScoreSign sg = score_sign(scale, kLog2e, kSignBf16x2);
     const int nkb = (N + kv::kBKV - 1) / kv::kBKV;
-    hipLaunchKernelGGL((kv::kernel<D, CAUSAL, MASK>), dim3((unsigned)((long long)B * H * nkb)), dim3(kv::kThreads), 0,
-                       stream, q, k, v, g, Dd, L2, dk, dv, H, N, nkb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
-    e = hipGetLastError();
+    e = launch_kernel(kv::kernel<D, CAUSAL, MASK>, dim3((unsigned)((long long)B * H * nkb)), dim3(kv::kThreads), 0,
+                      stream, q, k, v, g, Dd, L2, dk, dv, H, N, nkb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
     if (e != hipSuccess) return e;
     const int nqb = (N + qd::kBQ - 1) / qd::kBQ;
-    hipLaunchKernelGGL((qd::kernel<D, CAUSAL, MASK>), dim3((unsigned)((long long)B * H * nqb)), dim3(qd::kThreads), 0,
-                       stream, q, k, v, g, Dd, L2, dq, H, N, nqb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
-    return hipGetLastError();
+    return launch_kernel(qd::kernel<D, CAUSAL, MASK>, dim3((unsigned)((long long)B * H * nqb)), dim3(qd::kThreads), 0,
+                         stream, q, k, v, g, Dd, L2, dq, H, N, nqb, sg.c, scale, sg.and_mask, sg.xor_mask, kv_limit);
 }
 
 }  // namespace bwd

@@ -311,22 +311,18 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
     const bf16* V = static_cast<const bf16*>(v_cache);
     bf16* O = static_cast<bf16*>(o);
     if (max_splits > 0) {
-        if (d == 128)
-            hipLaunchKernelGGL((decode::split_kernel<128>), grid_split, dim3(decode::kThreads), 0, stream, Q, K, V,
-                               block_table, seq_lens, part_o, part_ml, H, max_pages, num_pages, max_splits, c);
-        else
-            hipLaunchKernelGGL((decode::split_kernel<64>), grid_split, dim3(decode::kThreads), 0, stream, Q, K, V,
-                               block_table, seq_lens, part_o, part_ml, H, max_pages, num_pages, max_splits, c);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e =
+            d == 128 ? launch_kernel(decode::split_kernel<128>, grid_split, dim3(decode::kThreads), 0, stream, Q, K, V,
+                                     block_table, seq_lens, part_o, part_ml, H, max_pages, num_pages, max_splits, c)
+                     : launch_kernel(decode::split_kernel<64>, grid_split, dim3(decode::kThreads), 0, stream, Q, K, V,
+                                     block_table, seq_lens, part_o, part_ml, H, max_pages, num_pages, max_splits, c);
         if (e != hipSuccess) return e;
     }
     if (d == 128)
-        hipLaunchKernelGGL((decode::combine_kernel<128>), dim3(grid_combine), dim3(decode::kThreads), 0, stream,
-                           part_o, part_ml, seq_lens, O, lse, H, max_pages, max_splits);
-    else
-        hipLaunchKernelGGL((decode::combine_kernel<64>), dim3(grid_combine), dim3(decode::kThreads), 0, stream,
-                           part_o, part_ml, seq_lens, O, lse, H, max_pages, max_splits);
-    return hipGetLastError();
+        return launch_kernel(decode::combine_kernel<128>, dim3(grid_combine), dim3(decode::kThreads), 0, stream,
+                             part_o, part_ml, seq_lens, O, lse, H, max_pages, max_splits);
+    return launch_kernel(decode::combine_kernel<64>, dim3(grid_combine), dim3(decode::kThreads), 0, stream, part_o,
+                         part_ml, seq_lens, O, lse, H, max_pages, max_splits);
 }
 
 }  // namespace fa

@@ -335,9 +335,8 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* o, float* l
     unsigned grid = 0;
     const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
-                       nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
-    return hipGetLastError();
+    return launch_kernel(fwd_kernel<D, CAUSAL, MASK>, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
+                         nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
 }
 
 }  // namespace fused_bf16

@@ -156,9 +156,8 @@ hipError_t launch(const float* q, const float* k, const float* v, float* o, floa
                   ScoreSign sg, const int32_t* kv_limit, hipStream_t stream) {
     const int nqb = (N + kBQ - 1) / kBQ;
     const dim3 grid((unsigned)((long long)B * H * nqb));
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK>), grid, dim3(kThreads), 0, stream, q, k, v, o, lse, H, N,
-                       nqb, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
-    return hipGetLastError();
+    return launch_kernel(fwd_kernel<D, CAUSAL, MASK>, grid, dim3(kThreads), 0, stream, q, k, v, o, lse, H, N, nqb,
+                         sg.c, sg.and_mask, sg.xor_mask, kv_limit);
 }
 
 }  // namespace fused_f32

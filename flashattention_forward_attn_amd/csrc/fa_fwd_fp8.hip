@@ -499,9 +499,8 @@ hipError_t launch(const uint8_t* qc, const int32_t* qe, const bf16* qb, const in
     unsigned grid = 0;
     const hipError_t e = walk_grid(items, !MASK, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MASK, QRAW>), dim3(grid), dim3(kThreads), 0, stream, qc, qe, qb, signs,
-                       kc, ke, v, o, lse, H, N, nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
-    return hipGetLastError();
+    return launch_kernel(fwd_kernel<D, CAUSAL, MASK, QRAW>, dim3(grid), dim3(kThreads), 0, stream, qc, qe, qb, signs,
+                         kc, ke, v, o, lse, H, N, nqb, (int)items, sg.c, sg.and_mask, sg.xor_mask, kv_limit);
 }
 
 }  // namespace fp8
@@ -513,9 +512,8 @@ hipError_t launch_fp8_quantize(const void* x, const int8_t* signs, uint8_t* code
     const dim3 grid((unsigned)((long long)B * H * nt));
 #define FA_QUANT(DD, TT)                                                                                    \
     if (d == DD && tile_rows == TT) {                                                                       \
-        hipLaunchKernelGGL((fp8::quant_kernel<DD, TT>), grid, dim3(fp8::kQuantThreads), 0, stream, X, signs, \
-                           codes, exps, N, nt);                                                             \
-        return hipGetLastError();                                                                           \
+        return launch_kernel(fp8::quant_kernel<DD, TT>, grid, dim3(fp8::kQuantThreads), 0, stream, X, signs, \
+                             codes, exps, N, nt);                                                           \
     }
     FA_QUANT(64, kFp8QTile)
     FA_QUANT(64, kFp8KTile)

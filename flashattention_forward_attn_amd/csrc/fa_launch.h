@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "fa_sizes.h"
 
 namespace fa {
@@ -31,6 +33,25 @@ inline ScoreSign score_sign(float scale, float factor, uint32_t sign_bits) {
 constexpr uint32_t kSignBf16x2 = 0x80008000u;
 constexpr uint32_t kSignF32 = 0x80000000u;
 constexpr uint32_t kSignE4m3x4 = 0x80808080u;
+
+// Launch `kernel` on `stream` and return the status of this launch alone.  (The
+// runtime's last-error slot, read after a <<<>>> launch, also holds any error an
+// earlier, unrelated runtime call left pending, which would then be reported as
+// this launch's.)
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
+                                A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    std::tuple<P...> values(static_cast<P>(args)...);
+    void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {};
+    std::apply(
+        [&ptrs](auto&... v) {
+            size_t i = 0;
+            ((ptrs[i++] = static_cast<void*>(&v)), ...);
+        },
+        values);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds_bytes, stream);
+}
 
 // Grid of a forward launch over `blocks` query blocks: with `walk`, one
 // workgroup per CU of the current device (never more than there are blocks),

@@ -278,19 +278,17 @@ __global__ __launch_bounds__(kThreads) void pv_f32(const float* __restrict__ P, 
 template <typename PT>
 hipError_t launch_softmax(const float* S, PT* P, float* lse, int B, int H, int N, int64_t ld, bool causal,
                           const int32_t* kv_limit, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)B * H * N));
+    const dim3 grid((unsigned)((int64_t)B * H * N)), block(kThreads);
     const int c = causal ? 1 : 0;
     if (ld <= 1 * kThreads)
-        hipLaunchKernelGGL((softmax_rows<PT, 1>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
-    else if (ld <= 4 * kThreads)
-        hipLaunchKernelGGL((softmax_rows<PT, 4>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
-    else if (ld <= 16 * kThreads)
-        hipLaunchKernelGGL((softmax_rows<PT, 16>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
-    else if (ld <= 64 * kThreads)
-        hipLaunchKernelGGL((softmax_rows<PT, 64>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
-    else
-        hipLaunchKernelGGL((softmax_rows<PT, 0>), grid, dim3(kThreads), 0, stream, S, P, lse, H, N, ld, c, kv_limit);
-    return hipGetLastError();
+        return launch_kernel(softmax_rows<PT, 1>, grid, block, 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    if (ld <= 4 * kThreads)
+        return launch_kernel(softmax_rows<PT, 4>, grid, block, 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    if (ld <= 16 * kThreads)
+        return launch_kernel(softmax_rows<PT, 16>, grid, block, 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    if (ld <= 64 * kThreads)
+        return launch_kernel(softmax_rows<PT, 64>, grid, block, 0, stream, S, P, lse, H, N, ld, c, kv_limit);
+    return launch_kernel(softmax_rows<PT, 0>, grid, block, 0, stream, S, P, lse, H, N, ld, c, kv_limit);
 }
 
 }  // namespace unfused
@@ -301,35 +299,32 @@ hipError_t launch_unfused(bool bf16_path, const void* q, const void* k, const vo
     using namespace unfused;
     const int64_t ld = unfused_ld(N);
     const unsigned BH = (unsigned)((int64_t)B * H);
+    const dim3 block(kThreads);
     hipError_t err;
     if (bf16_path) {
+        const bf16 *Q = static_cast<const bf16*>(q), *K = static_cast<const bf16*>(k);
         const dim3 g1((N + kScoreTile - 1) / kScoreTile, (N + kScoreTile - 1) / kScoreTile, BH);
-        if (d == 64)
-            hipLaunchKernelGGL((scores_bf16<64>), g1, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, S, N, ld, scale);
-        else
-            hipLaunchKernelGGL((scores_bf16<128>), g1, dim3(kThreads), 0, stream, (const bf16*)q, (const bf16*)k, S, N, ld, scale);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        err = d == 64 ? launch_kernel(scores_bf16<64>, g1, block, 0, stream, Q, K, S, N, ld, scale)
+                      : launch_kernel(scores_bf16<128>, g1, block, 0, stream, Q, K, S, N, ld, scale);
+        if (err != hipSuccess) return err;
         if ((err = launch_softmax<bf16>(S, (bf16*)P, lse, B, H, N, ld, causal, kv_limit, stream)) != hipSuccess) return err;
+        const bf16 *Pb = static_cast<const bf16*>(P), *Vb = static_cast<const bf16*>(v);
+        bf16* Ob = static_cast<bf16*>(o);
         const dim3 g3((N + 127) / 128, BH);
-        if (d == 64)
-            hipLaunchKernelGGL((pv_bf16<64>), g3, dim3(kThreads), 0, stream, (const bf16*)P, (const bf16*)v, (bf16*)o, N, ld);
-        else
-            hipLaunchKernelGGL((pv_bf16<128>), g3, dim3(kThreads), 0, stream, (const bf16*)P, (const bf16*)v, (bf16*)o, N, ld);
-        return hipGetLastError();
+        return d == 64 ? launch_kernel(pv_bf16<64>, g3, block, 0, stream, Pb, Vb, Ob, N, ld)
+                       : launch_kernel(pv_bf16<128>, g3, block, 0, stream, Pb, Vb, Ob, N, ld);
     }
+    const float *Q = static_cast<const float*>(q), *K = static_cast<const float*>(k);
     const dim3 g1((unsigned)(((int64_t)N * N + kThreads - 1) / kThreads), BH);
-    if (d == 64)
-        hipLaunchKernelGGL((scores_f32<64>), g1, dim3(kThreads), 0, stream, (const float*)q, (const float*)k, S, N, ld, scale);
-    else
-        hipLaunchKernelGGL((scores_f32<128>), g1, dim3(kThreads), 0, stream, (const float*)q, (const float*)k, S, N, ld, scale);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = d == 64 ? launch_kernel(scores_f32<64>, g1, block, 0, stream, Q, K, S, N, ld, scale)
+                  : launch_kernel(scores_f32<128>, g1, block, 0, stream, Q, K, S, N, ld, scale);
+    if (err != hipSuccess) return err;
     if ((err = launch_softmax<float>(S, (float*)P, lse, B, H, N, ld, causal, kv_limit, stream)) != hipSuccess) return err;
+    const float *Pf = static_cast<const float*>(P), *Vf = static_cast<const float*>(v);
+    float* Of = static_cast<float*>(o);
     const dim3 g3((unsigned)(((int64_t)N * d + kThreads - 1) / kThreads), BH);
-    if (d == 64)
-        hipLaunchKernelGGL((pv_f32<64>), g3, dim3(kThreads), 0, stream, (const float*)P, (const float*)v, (float*)o, N, ld);
-    else
-        hipLaunchKernelGGL((pv_f32<128>), g3, dim3(kThreads), 0, stream, (const float*)P, (const float*)v, (float*)o, N, ld);
-    return hipGetLastError();
+    return d == 64 ? launch_kernel(pv_f32<64>, g3, block, 0, stream, Pf, Vf, Of, N, ld)
+                   : launch_kernel(pv_f32<128>, g3, block, 0, stream, Pf, Vf, Of, N, ld);
 }
 
 }  // namespace fa
