@@ -57,6 +57,7 @@ import numpy as np
 
 HEADLINE = "bf16_causal_b2h32n4096d128"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3  # dense fp32 MFMA
 PEAK_SCLK_MHZ = 2400.0  # the clock the published peaks assume
 METRIC = "attention fwd TFLOP/s (bf16, causal/non-causal) and % of MI355X MFMA peak"
 BWD_METRIC = "attention bwd TFLOP/s (bf16, nominal 10*N^2*d per head) and % of MI355X MFMA peak"
@@ -72,7 +73,8 @@ PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 # the host live in fa_sizes.h.)
 KERNEL_SOURCES = {
     "fused": ["fa_fwd_bf16.hip", "fa_tile.h", "fa_common.h"],
-    "unfused": ["fa_unfused.hip", "fa_common.h"],
+    "fused_f32": ["fa_fwd_f32.hip", "fa_common.h"],
+    "unfused": ["fa_unfused.hip", "fa_tile.h", "fa_common.h"],
     "backward": ["fa_bwd_bf16.hip", "fa_tile.h", "fa_common.h"],
     "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_sizes.h"],
     "fp8": ["fa_fwd_fp8.hip", "fa_tile.h", "fa_common.h", "fa_sizes.h"],
@@ -223,14 +225,15 @@ def fused_launcher(torch, binding, x):
     return launch
 
 
-def measure_fused(torch, binding, x, steps, warmup, spread=0, clock=False, launch=None):
+def measure_fused(torch, binding, x, steps, warmup, spread=0, clock=None, launch=None):
     """Mean ms per fused launch; with spread > 0 also launch_spread over that many
-    launches (and with clock the shader clock sampled while the kernel runs on)."""
+    launches; with clock given (True or False) a third value, the shader clock
+    sampled while the kernel runs on (None when clock is False)."""
     launch = launch or fused_launcher(torch, binding, x)
     ms = time_launches(torch, launch, steps, warmup)
     sp = launch_spread(torch, launch, spread) if spread else None
     clk = sample_sclk(torch, launch) if clock else None
-    if clock:
+    if clock is not None:
         return ms, sp, clk
     return (ms, sp) if spread else ms
 
@@ -492,13 +495,14 @@ def cpu_baseline_backward(x, g):
     }
 
 
-def load_traffic(path_file: str, path: str, workload: str):
-    """Measured HBM bytes per launch for (path, workload), or None if absent or stale."""
+def load_traffic(path_file: str, path: str, workload: str, sources: str | None = None):
+    """Measured HBM bytes per launch for (path, workload), or None if absent or
+    stale (taken on other kernel sources: those of `sources`, default `path`)."""
     if not os.path.exists(path_file):
         return None
     with open(path_file) as f:
         t = json.load(f).get(path, {}).get(workload)
-    if t and t.get("kernel_source_sha256") == _kernel_digest(path):
+    if t and t.get("kernel_source_sha256") == _kernel_digest(sources or path):
         return t.get("bytes_per_launch")
     return None
 
@@ -558,6 +562,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the unfused baseline and other workloads")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample after the timed steps (about a second of extra launches; "
+                         "for runs under a profiler)")
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 FETCH_SIZE/WRITE_SIZE), if present")
@@ -566,8 +573,9 @@ def main() -> int:
                          "backward pass, the paged decode or the FP8 forward as the step")
     ap.add_argument("--decode-workload", default=DECODE_HEADLINE)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of this many MiB (twice) and exit; "
-                         "its FETCH_SIZE/WRITE_SIZE calibrate the traffic counters")
+                    help="only run a plain device-to-device copy of this many MiB (twice untimed, "
+                         "then 13 timed for its TB/s) and exit; its FETCH_SIZE/WRITE_SIZE calibrate the "
+                         "traffic counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -589,7 +597,12 @@ def main() -> int:
         for _ in range(2):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+        # the same copy timed: a read+write stream, the practical ceiling for kernels
+        # that read and write about as much (the unfused softmax)
+        ms = time_launches(torch, lambda: dst.copy_(src), 10, 3)
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "copy_ms": round(ms, 4), "copy_TBps_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e12, 3)}),
+              flush=True)
         return 0
     binding.load()
 
@@ -646,7 +659,7 @@ def main() -> int:
         tflops = w.bwd_flops() / (ms * 1e-3) / 1e12
     elif args.path == "fused":
         ms, spread, clock = measure_fused(torch, binding, x, args.steps, args.warmup, spread=SPREAD_LAUNCHES,
-                                          clock=True, launch=launch)
+                                          clock=not args.no_clock, launch=launch)
         host_us = LAST_HOST_US[0]
         tflops = w.flops() / (ms * 1e-3) / 1e12
     else:
@@ -655,7 +668,9 @@ def main() -> int:
     # host work only after every timed GPU leg
     for job in deferred:
         job()
-    traffic = load_traffic(args.traffic, args.path, w.name)
+    traffic = load_traffic(args.traffic, args.path, w.name,
+                           "fused_f32" if args.path == "fused" and w.dtype == "f32" else None)
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" and args.path == "fused" else PEAK_BF16_TFLOPS
 
     line = {
         "metric": BWD_METRIC if args.path == "backward" else METRIC,
@@ -674,14 +689,14 @@ def main() -> int:
                    "scale": "1/sqrt(d)",
                    "flops_per_step": w.bwd_flops() if args.path == "backward" else w.flops(), "path": args.path,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
     }
     if clock is not None:
         # the same fraction against the MFMA peak at the clock the GPU ran at
         line["roofline"]["clock"] = clock
         line["roofline"]["frac_at_measured_clock"] = round(
-            tflops / (PEAK_BF16_TFLOPS * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ), 4)
+            tflops / (peak * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ), 4)
     if spread is not None:
         fl = w.bwd_flops() if args.path == "backward" else w.flops()
         spread["TFLOP/s_at_median"] = round(fl / (spread["median_ms"] * 1e-3) / 1e12, 2)

@@ -91,6 +91,10 @@ fa_status unfused(bool bf16_path, const void* q, const void* k, const void* v, v
     if (st != FA_OK) return st;
     if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;  // grid y/z limit of the unfused kernels
     if (N > kUnfusedMaxN) return FA_ERR_SHAPE;         // 32-bit offsets into one head's P
+    // the softmax launch runs 64, 256 or 512 threads per row (up to 4096, up to
+    // 16384, more keys per row); a grid holds fewer than 2^32 work-items
+    const int64_t ld = fa::unfused_ld(N), per_row = ld <= 4096 ? 64 : (ld <= 16384 ? 256 : 512);
+    if ((int64_t)B * H * N * per_row > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
     const size_t need = workspace_bytes(B, H, N, elem);
     if (!workspace || need == 0 || workspace_bytes_given < need || !aligned(workspace, kWsAlign))
         return FA_ERR_WORKSPACE;
@@ -100,7 +104,7 @@ fa_status unfused(bool bf16_path, const void* q, const void* k, const void* v, v
                     span(lse, (int64_t)B * H * N * 4), span(kv_limit, kv_limit ? (int64_t)B * N * 4 : 0)}) {
         if (overlap(rw, r)) return FA_ERR_ALIAS;
     }
-    const size_t rows = (size_t)B * H * N * (size_t)fa::unfused_ld(N);
+    const size_t rows = (size_t)B * H * N * (size_t)ld;
     float* S = static_cast<float*>(workspace);
     void* P = static_cast<char*>(workspace) + round_up(rows * 4, kWsAlign);
     return hip_status(fa::launch_unfused(bf16_path, q, k, v, o, lse, B, H, N, d, causal != 0, scale, kv_limit, S, P,
