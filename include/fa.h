@@ -253,7 +253,8 @@ fa_status fa_decode_paged_bf16(const fa_bf16 *q, const fa_bf16 *k_cache, const f
  * what its own first kernel wrote.  Calls on one stream are ordered; calls that
  * may overlap on one GPU (different streams, or host threads without ordering)
  * race on the buffer and must not be made.  The first call on a device looks up
- * the buffer's device address there (FA_ERR_HIP if that fails).
+ * the buffer's device address there (FA_ERR_HIP if that fails); a caller that
+ * captures the call into a HIP graph makes one call outside the capture first.
  */
 fa_status fa_decode_paged_bf16_noalloc(const fa_bf16 *q, const fa_bf16 *k_cache, const fa_bf16 *v_cache,
                                        const int32_t *block_table, const int32_t *seq_lens,

@@ -2,7 +2,8 @@
 
 None of them allocates, synchronises or issues a memset, so a caller in a
 serving loop can capture them once and replay: here the fused forward, the
-backward pass, the paged decode and the FP8 forward are each captured on
+backward pass, the paged decode (with and without a workspace) and the FP8
+forward are each captured on
 torch's capture stream, replayed several times with eager work and
 synchronisation in between (the inputs change between replays), and every
 replay is compared bit for bit with an eager call on the same inputs.
@@ -98,6 +99,32 @@ def test_decode_graph():
 
     def refill(r):  # new queries and new lengths each replay, as a decode loop would have
         rng = np.random.default_rng(r)
+        q.copy_(bf16(torch, inputs.bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))))
+        sl.copy_(torch.from_numpy(rng.integers(0, w.max_len + 1, size=w.B).astype(np.int32)))
+
+    def eager():
+        return list(binding.decode_paged(q, kc, vc, bt, sl, scale=w.scale))
+
+    replay_and_compare(torch, graph, refill, eager, [o, lse])
+
+
+def test_decode_noalloc_graph():
+    """The no-allocation decode, the entry point meant for captured loops: every
+    replay equals the workspace entry point's eager result."""
+    torch = cuda()
+    w = inputs.DecodeWorkload("graph_dec_na", 5, 4, 64, 900, seed=8)
+    x = inputs.generate_decode(w)
+    q, kc, vc = bf16(torch, x.q_bits), bf16(torch, x.k_bits), bf16(torch, x.v_bits)
+    bt = torch.from_numpy(x.block_table).cuda()
+    sl = torch.from_numpy(x.seq_lens).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+
+    graph = capture(torch, lambda: binding.fa_decode_paged_bf16_noalloc(q, kc, vc, bt, sl, o, lse, w.scale,
+                                                                       torch.cuda.current_stream()))
+
+    def refill(r):
+        rng = np.random.default_rng(50 + r)
         q.copy_(bf16(torch, inputs.bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))))
         sl.copy_(torch.from_numpy(rng.integers(0, w.max_len + 1, size=w.B).astype(np.int32)))
 
