@@ -159,35 +159,44 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const size_t head = (size_t)cur.bh * N * D;
         const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
         const int qrow = cur.q0 + w * kQPW + col;
+        // Q's raw bits go out first and stay in flight across the first barrier,
+        // landing together with the key limits and the first K/V tile: one memory
+        // latency per block, not three in a row.
+        u32x4 qraw[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qraw[kk] = qrow < N ? *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half)
+                                : u32x4{};
         const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
         const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
         // block_max alternates between two rows, so a fast wave writing the next
         // item's entry never meets a slow wave still reading this one's
         if (lane == 0) block_max[r & 1][w] = wmax;
 
-        bf16x8 qf[D / 16];
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            if (qrow < N) {
-                // the scale's sign folded into Q (see ScoreSign)
-                u32x4 u = *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], q_and, q_xor);
-                qf[kk] = __builtin_bit_cast(bf16x8, u);
-            } else {
-                qf[kk] = bf16x8{};
-            }
-        }
-        // after this barrier no wave reads the previous item's stages any more
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) launder(qf[kk]);
+        // After this barrier no wave reads the previous item's stages any more, and
+        // every wave's block_max entry is written.  It orders LDS only (a full
+        // __syncthreads would first wait for the Q loads and the previous item's
+        // output stores); the empty asm statements keep the compiler from moving
+        // memory accesses across it.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         int kv_end = 0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[r & 1][i]);
         const int ntiles = (kv_end + kBK - 1) / kBK;
         if (ntiles > 0) dma_tile(kdesc, vdesc, 0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        bf16x8 qf[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 u = qraw[kk];
+            // the scale's sign folded into Q (see ScoreSign)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], q_and, q_xor);
+            qf[kk] = __builtin_bit_cast(bf16x8, u);
+            launder(qf[kk]);
+        }
         __syncthreads();
 
         f32x16 oacc[D / 32];
