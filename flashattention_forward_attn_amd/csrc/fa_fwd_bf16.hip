@@ -316,18 +316,17 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         // Epilogue: one division per row; each lane half summed its own keys.
         const float l_tot = halves_sum(l_sum);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        // O leaves in 16-byte stores (8 consecutive dims per lane, see o_rows16)
+        u32x4 ov[D / 32][2];
+#pragma unroll
+        for (int d32 = 0; d32 < D / 32; ++d32) o_rows16(oacc[d32], inv, ov[d32]);
         if (qrow < N) {
             bf16* orow = O + head + (size_t)qrow * D;
 #pragma unroll
             for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int dim = 32 * d32 + 8 * gq + 4 * half;
-                    u32x2 out;
-                    out.x = pack_bf16x2(oacc[d32][4 * gq + 0] * inv, oacc[d32][4 * gq + 1] * inv);
-                    out.y = pack_bf16x2(oacc[d32][4 * gq + 2] * inv, oacc[d32][4 * gq + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + dim) = out;
-                }
+                for (int p = 0; p < 2; ++p)
+                    *reinterpret_cast<u32x4*>(orow + 32 * d32 + 16 * p + 8 * half) = ov[d32][p];
             if (half == 0)
                 LSE[(size_t)cur.bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
         }

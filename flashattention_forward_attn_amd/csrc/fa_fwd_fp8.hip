@@ -472,18 +472,17 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
 
         const float l_tot = halves_sum(l_sum);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        // O leaves in 16-byte stores (8 consecutive dims per lane, see o_rows16)
+        u32x4 ov[D / 32][2];
+#pragma unroll
+        for (int d32 = 0; d32 < D / 32; ++d32) o_rows16(oacc[d32], inv, ov[d32]);
         if (qrow < N) {
             bf16* orow = O + ((size_t)bh * N + qrow) * D;
 #pragma unroll
             for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int dim = 32 * d32 + 8 * g + 4 * half;
-                    u32x2 out;
-                    out.x = pack_bf16x2(oacc[d32][4 * g + 0] * inv, oacc[d32][4 * g + 1] * inv);
-                    out.y = pack_bf16x2(oacc[d32][4 * g + 2] * inv, oacc[d32][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + dim) = out;
-                }
+                for (int p = 0; p < 2; ++p)
+                    *reinterpret_cast<u32x4*>(orow + 32 * d32 + 16 * p + 8 * half) = ov[d32][p];
             if (half == 0)
                 LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
