@@ -54,6 +54,7 @@
 //     gets its own workgroup and the hardware balances them.
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_epilogue.h"
 #include "fa_tile.h"
 
 namespace fa {

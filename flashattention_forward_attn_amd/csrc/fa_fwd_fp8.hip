@@ -25,6 +25,7 @@
 //      comes out already scaled.  V stays bf16.
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_epilogue.h"
 #include "fa_tile.h"
 
 namespace fa {

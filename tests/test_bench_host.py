@@ -3,6 +3,7 @@ stored traffic figure is reported only while the kernel sources it was measured
 on are unchanged."""
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -27,6 +28,31 @@ def test_kernel_sources_exist(path):
     for name in bench.KERNEL_SOURCES[path]:
         assert os.path.isfile(os.path.join(here, name)), name
     assert len(bench._kernel_digest(path)) == 64
+
+
+@pytest.mark.parametrize("path", sorted(bench.KERNEL_SOURCES))
+def test_kernel_sources_cover_the_included_headers(path):
+    """A recorded traffic figure is voided by any change to the code its kernel is
+    built from, so every header the kernel source includes must be hashed with it.
+    Exceptions: fa_launch.h declares host launchers only, and fa_sizes.h (reached
+    through it) counts only where the kernel uses one of its constants."""
+    here = os.path.join(ROOT, "flashattention_forward_attn_amd", "csrc")
+    text = lambda name: open(os.path.join(here, name)).read()
+
+    def includes(name, seen):
+        for h in re.findall(r'^#include "([^"]+)"', text(name), re.M):
+            if h not in seen:
+                seen.add(h)
+                includes(h, seen)
+        return seen
+
+    main = bench.KERNEL_SOURCES[path][0]
+    need = includes(main, set()) - {"fa_launch.h", "fa_sizes.h"}
+    sizes = re.findall(r"constexpr\s+\w+\s+(k\w+)\s*=", text("fa_sizes.h"))
+    assert sizes
+    if any(re.search(rf"\b{n}\b", text(main)) for n in sizes):
+        need.add("fa_sizes.h")
+    assert need <= set(bench.KERNEL_SOURCES[path]), sorted(need - set(bench.KERNEL_SOURCES[path]))
 
 
 def test_traffic_reported_only_for_current_sources(tmp_path):
