@@ -160,15 +160,24 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const size_t head = (size_t)cur.bh * N * D;
         const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
         const int qrow = cur.q0 + w * kQPW + col;
-        // Q's raw bits go out first and stay in flight across the first barrier,
-        // landing together with the key limits and the first K/V tile: one memory
-        // latency per block, not three in a row.
+        // The key limit, which the first barrier needs, goes out first and Q's raw
+        // bits right behind it.  Loads complete in order, so the wait before the
+        // barrier covers the limit alone, and Q stays in flight until the first K/V
+        // tile lands.  Both go through buffer descriptors, rows past N at an offset
+        // past the end (they read as zeros), so no load sits in a branch: with
+        // branches the compiler waited for the first loads before issuing the rest.
+        int lraw = 0;  // this row's key limit as stored (rows past N read 0)
+        if constexpr (MASK)
+            lraw = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(kv_limit + (size_t)b * N, (uint32_t)N * 4u),
+                                                        qrow < N ? qrow * 4 : N * 4, 0, 0);
+        const auto qrs = buffer_rsrc(Q + head, head_bytes);
+        const uint32_t qoff = ((uint32_t)qrow * D + 8 * half) * 2u;
         u32x4 qraw[D / 16];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
-            qraw[kk] = qrow < N ? *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half)
-                                : u32x4{};
-        const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
+            qraw[kk] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, qrow < N ? qoff + 32 * kk : head_bytes, 0, 0));
+        const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? &lraw : nullptr);
         const int wmax = wave_max_i(lim), wmin = wave_min_i(lim);
         // block_max alternates between two rows, so a fast wave writing the next
         // item's entry never meets a slow wave still reading this one's
