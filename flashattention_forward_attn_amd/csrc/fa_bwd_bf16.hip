@@ -28,6 +28,7 @@
 // computing S and dP twice.
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_epilogue.h"
 #include "fa_tile.h"
 
 namespace fa {
@@ -373,22 +374,23 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
         st = nst;
     }
 
-    // Epilogue: lane holds key kcol, dims 32 d32 + 8 g + 4 half .. +3 in registers 4 g ..
+    // Epilogue: lane holds key kcol, dims 32 d32 + 8 g + 4 half .. +3 in registers 4 g ..;
+    // dK and dV leave in 16-byte stores (8 consecutive dims per lane, see o_rows16)
+    u32x4 ko[D / 32][2], vo[D / 32][2];
+#pragma unroll
+    for (int d32 = 0; d32 < D / 32; ++d32) {
+        o_rows16(dkacc[d32], scale, ko[d32]);
+        o_rows16(dvacc[d32], 1.0f, vo[d32]);
+    }
     if (kcol < N) {
         bf16* krow = dK + head + (size_t)kcol * D;
         bf16* vrow = dV + head + (size_t)kcol * D;
 #pragma unroll
         for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dim = 32 * d32 + 8 * g + 4 * half;
-                u32x2 ko, vo;
-                ko.x = pack_bf16x2(dkacc[d32][4 * g + 0] * scale, dkacc[d32][4 * g + 1] * scale);
-                ko.y = pack_bf16x2(dkacc[d32][4 * g + 2] * scale, dkacc[d32][4 * g + 3] * scale);
-                vo.x = pack_bf16x2(dvacc[d32][4 * g + 0], dvacc[d32][4 * g + 1]);
-                vo.y = pack_bf16x2(dvacc[d32][4 * g + 2], dvacc[d32][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(krow + dim) = ko;
-                *reinterpret_cast<u32x2*>(vrow + dim) = vo;
+            for (int p = 0; p < 2; ++p) {
+                *reinterpret_cast<u32x4*>(krow + 32 * d32 + 16 * p + 8 * half) = ko[d32][p];
+                *reinterpret_cast<u32x4*>(vrow + 32 * d32 + 16 * p + 8 * half) = vo[d32][p];
             }
     }
 }
@@ -576,18 +578,16 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
         __syncthreads();
     }
 
+    // dQ leaves in 16-byte stores (8 consecutive dims per lane, see o_rows16)
+    u32x4 qo[D / 32][2];
+#pragma unroll
+    for (int d32 = 0; d32 < D / 32; ++d32) o_rows16(dqacc[d32], scale, qo[d32]);
     if (qrow < N) {
         bf16* row = dQ + head + (size_t)qrow * D;
 #pragma unroll
         for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dim = 32 * d32 + 8 * g + 4 * half;
-                u32x2 out;
-                out.x = pack_bf16x2(dqacc[d32][4 * g + 0] * scale, dqacc[d32][4 * g + 1] * scale);
-                out.y = pack_bf16x2(dqacc[d32][4 * g + 2] * scale, dqacc[d32][4 * g + 3] * scale);
-                *reinterpret_cast<u32x2*>(row + dim) = out;
-            }
+            for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4*>(row + 32 * d32 + 16 * p + 8 * half) = qo[d32][p];
     }
 }
 }  // namespace qd

@@ -1,12 +1,13 @@
-// fa_epilogue.h -- the output stage shared by the two fused forward kernels
-// (bf16 and FP8 scores), which accumulate O^T so that each lane owns one query.
+// fa_epilogue.h -- the output stage shared by the kernels whose 32x32 MFMA
+// accumulators hold one output row per lane: O in the two fused forward kernels
+// (bf16 and FP8 scores), dK, dV and dQ in the backward.
 #pragma once
 #include "fa_common.h"
 
 namespace fa {
 
-// Output rows of the kernels that accumulate O^T: lane half h holds dims
-// 8 g + 4 h .. +3 of a 32-dim block of its query in acc[4 g .. 4 g + 3] (g = 0..3).
+// Lane half h holds dims 8 g + 4 h .. +3 of a 32-dim block of its row in
+// acc[4 g .. 4 g + 3] (g = 0..3).
 // Scales them by inv, packs them to bf16 and hands back out[p] = dims 16 p + 8 h ..
 // +7, ready for one 16-byte store each: for every pair of groups (2 p, 2 p + 1) one
 // v_permlane32_swap per word, which trades the upper lanes of its first operand
