@@ -74,7 +74,7 @@ PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 KERNEL_SOURCES = {
     "fused": ["fa_fwd_bf16.hip", "fa_epilogue.h", "fa_tile.h", "fa_common.h"],
     "fused_f32": ["fa_fwd_f32.hip", "fa_common.h"],
-    "unfused": ["fa_unfused.hip", "fa_tile.h", "fa_common.h"],
+    "unfused": ["fa_unfused.hip", "fa_epilogue.h", "fa_tile.h", "fa_common.h"],
     "backward": ["fa_bwd_bf16.hip", "fa_epilogue.h", "fa_tile.h", "fa_common.h"],
     "decode": ["fa_decode_bf16.hip", "fa_common.h", "fa_sizes.h"],
     "fp8": ["fa_fwd_fp8.hip", "fa_epilogue.h", "fa_tile.h", "fa_common.h", "fa_sizes.h"],

@@ -1,6 +1,6 @@
 // fa_epilogue.h -- the output stage shared by the kernels whose 32x32 MFMA
 // accumulators hold one output row per lane: O in the two fused forward kernels
-// (bf16 and FP8 scores), dK, dV and dQ in the backward.
+// (bf16 and FP8 scores) and in the unfused P V, dK, dV and dQ in the backward.
 #pragma once
 #include "fa_common.h"
 

@@ -17,6 +17,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_epilogue.h"
 #include "fa_tile.h"
 
 namespace fa {
@@ -374,17 +375,16 @@ __global__ __launch_bounds__(kPvThreads) void pv_bf16(const bf16* __restrict__ P
         });
     }
     const int q = r0 + prow;
+    // O leaves in 16-byte stores (8 consecutive dims per lane, see o_rows16)
+    u32x4 ov[D / 32][2];
+#pragma unroll
+    for (int d32 = 0; d32 < D / 32; ++d32) o_rows16(acc[d32], 1.0f, ov[d32]);
     if (q < N) {
         bf16* orow = O + bh * N * D + (size_t)q * D;
 #pragma unroll
         for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int dim = 32 * d32 + 8 * gq + 4 * half;
-                *reinterpret_cast<u32x2*>(orow + dim) =
-                    u32x2{pack_bf16x2(acc[d32][4 * gq + 0], acc[d32][4 * gq + 1]),
-                          pack_bf16x2(acc[d32][4 * gq + 2], acc[d32][4 * gq + 3])};
-            }
+            for (int p = 0; p < 2; ++p) *reinterpret_cast<u32x4*>(orow + 32 * d32 + 16 * p + 8 * half) = ov[d32][p];
     }
 }
 
