@@ -457,38 +457,40 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
         }
     };
 
+    // The row's key limit goes out first (the first barrier needs it; loads
+    // complete in order), then Q, dO and the row statistics, which stay in flight
+    // across that barrier and land together with the first K/V tile.  All through
+    // buffer descriptors, rows past N at an offset past the end (they read zeros),
+    // so no load sits in a branch and none waits for another.
     const int qrow = qb * kBQ + w * kQPW + col;
-    const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? kv_limit + (size_t)b * N + qrow : nullptr);
+    const bool in = qrow < N;
+    int lraw = 0;  // the stored key limit of this row
+    if constexpr (MASK)
+        lraw = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(kv_limit + (size_t)b * N, (uint32_t)N * 4u),
+                                                    in ? qrow * 4 : N * 4, 0, 0);
+    const auto qrs = buffer_rsrc(Q + head, head_bytes), grs = buffer_rsrc(dO + head, head_bytes);
+    const uint32_t roff = ((uint32_t)qrow * D + 8 * half) * 2u;
+    u32x4 qraw[D / 16], graw[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const uint32_t off = in ? roff + 32 * kk : head_bytes;
+        qraw[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+        graw[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
+    }
+    const int soff = in ? qrow * 4 : N * 4;
+    const float l2_in = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(L2 + (size_t)bh * N, (uint32_t)N * 4u), soff, 0, 0));
+    const float dd = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(Dd + (size_t)bh * N, (uint32_t)N * 4u), soff, 0, 0));
+    const int lim = row_key_limit(qrow, N, CAUSAL, MASK ? &lraw : nullptr);
     const int wmax = __builtin_amdgcn_readfirstlane(wave_max_i(lim));
     const int wmin = __builtin_amdgcn_readfirstlane(wave_min_i(lim));
     if (lane == 0) block_max[w] = wmax;
-
-    bf16x8 qf[D / 16], gf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        if (qrow < N) {
-            // the scale's sign folded into Q, the scores' register operand (see ScoreSign)
-            u32x4 u = *reinterpret_cast<const u32x4*>(Q + head + (size_t)qrow * D + 16 * kk + 8 * half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], s_and, s_xor);
-            qf[kk] = __builtin_bit_cast(bf16x8, u);
-            gf[kk] = *reinterpret_cast<const bf16x8*>(dO + head + (size_t)qrow * D + 16 * kk + 8 * half);
-        } else {
-            qf[kk] = bf16x8{};
-            gf[kk] = bf16x8{};
-        }
-    }
-    float l2 = INFINITY, dd = 0.f;
-    if (qrow < N) {
-        l2 = L2[(size_t)bh * N + qrow];
-        dd = Dd[(size_t)bh * N + qrow];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        launder(qf[kk]);
-        launder(gf[kk]);
-    }
+    // every wave's block_max entry is written; LDS only (a full __syncthreads
+    // would first wait for the loads above)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     int kv_end = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) kv_end = max(kv_end, block_max[i]);
@@ -522,6 +524,19 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
 
     if (ntiles > 0) dma_tile(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the scale's sign folded into Q, the scores' register operand (see ScoreSign)
+    bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 u = qraw[kk];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = score_signed(u[e], s_and, s_xor);
+        qf[kk] = __builtin_bit_cast(bf16x8, u);
+        gf[kk] = __builtin_bit_cast(bf16x8, graw[kk]);
+        launder(qf[kk]);
+        launder(gf[kk]);
+    }
+    const float l2 = in ? l2_in : INFINITY;  // a row past N sees no key
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
