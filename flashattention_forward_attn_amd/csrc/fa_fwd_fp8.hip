@@ -48,6 +48,26 @@ __device__ __forceinline__ int tile_exponent(float a) {
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// The value lane l ^ hb holds (hb = 1, 2, 4 or 8), from within l's 16-lane DPP row:
+// quad_perm swaps for 1 and 2; row_half_mirror (l ^ 7) after a quad reversal (l ^ 3)
+// for 4, and after row_mirror (l ^ 15) for 8.  No LDS access and no wait.
+__device__ __forceinline__ float xor_lanes(float v, int hb) {
+    int u = __builtin_bit_cast(int, v);
+    switch (hb) {
+        case 1: u = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, false); break;  // quad_perm 1 0 3 2
+        case 2: u = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, false); break;  // quad_perm 2 3 0 1
+        case 4:
+            u = __builtin_amdgcn_update_dpp(0, u, 0x1B, 0xF, 0xF, false);   // quad_perm 3 2 1 0
+            u = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, false);  // row_half_mirror
+            break;
+        default:
+            u = __builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, false);  // row_mirror
+            u = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, false);  // row_half_mirror
+            break;
+    }
+    return __builtin_bit_cast(float, u);
+}
+
 template <int D, int T>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __restrict__ x,
                                                               const int8_t* __restrict__ signs,
@@ -64,6 +84,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __rest
     const int tile = blockIdx.x % nt;
     const int rp = tid / LPR, cidx = tid % LPR;
 
+    // Every pass's 16 bytes go out at once, through a buffer descriptor over this
+    // (batch, head)'s rows; rows past the tile or past N sit at an offset past its
+    // end and read zeros, so no load sits in a branch or waits for another.
+    const uint32_t head_bytes = (uint32_t)N * D * 2u;
+    const auto xrs = buffer_rsrc(x + bh * N * D, head_bytes);
+    u32x4 raw[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int rin = p * RPP + rp, row = tile * T + rin;
+        const bool ok = rin < T && row < N;
+        raw[p] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? ((uint32_t)row * D + 8 * cidx) * 2u : head_bytes, 0, 0));
+    }
     float sg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = (float)signs[8 * cidx + e];
@@ -74,8 +107,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __rest
     for (int p = 0; p < PASSES; ++p) {
         const int rin = p * RPP + rp, row = tile * T + rin;
         const bool ok = rin < T && row < N;
-        bf16x8 v = bf16x8{};
-        if (ok) v = *reinterpret_cast<const bf16x8*>(x + (bh * N + row) * D + 8 * cidx);
+        const bf16x8 v = __builtin_bit_cast(bf16x8, raw[p]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[p][e] = (float)v[e] * sg[e];
         // butterfly stages inside the lane: dims 8 cidx + i, pairs (i, i + h)
@@ -93,7 +125,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const bf16* __rest
         for (int hb = 1; hb < LPR; hb <<= 1)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float other = __shfl_xor(y[p][i], hb, kWave);
+                const float other = xor_lanes(y[p][i], hb);
                 y[p][i] = (cidx & hb) ? other - y[p][i] : y[p][i] + other;
             }
         if (ok)
