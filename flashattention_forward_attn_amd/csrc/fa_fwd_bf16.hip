@@ -160,12 +160,13 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const size_t head = (size_t)cur.bh * N * D;
         const i32x4 kdesc = dma_desc(K + head, head_bytes), vdesc = dma_desc(V + head, head_bytes);
         const int qrow = cur.q0 + w * kQPW + col;
-        // The key limit, which the first barrier needs, goes out first and Q's raw
-        // bits right behind it.  Loads complete in order, so the wait before the
-        // barrier covers the limit alone, and Q stays in flight until the first K/V
-        // tile lands.  Both go through buffer descriptors, rows past N at an offset
-        // past the end (they read as zeros), so no load sits in a branch: with
-        // branches the compiler waited for the first loads before issuing the rest.
+        // With key limits, this row's limit (which the first barrier needs) goes out
+        // first and Q's raw bits right behind it: loads complete in order, so the
+        // wait before the barrier covers the limit alone.  Q stays in flight until
+        // the first K/V tile lands.  Both go through buffer descriptors, rows past N
+        // at an offset past the end (they read as zeros), so no load sits in a
+        // branch: with branches the compiler waited for the first loads before
+        // issuing the rest.
         int lraw = 0;  // this row's key limit as stored (rows past N read 0)
         if constexpr (MASK)
             lraw = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(kv_limit + (size_t)b * N, (uint32_t)N * 4u),
