@@ -213,7 +213,8 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         f32x16 oacc[D / 32];
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-        float m_ref = -INFINITY, l_sum = 0.f;
+        float m_ref = -INFINITY;
+        float l_sum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: four short dependency chains
 
         auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
             constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
@@ -253,17 +254,20 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                             if (key >= lim) s[sub][rr] = -INFINITY;
                         }
                 }
-                float mx = -INFINITY;
+                // four independent partial maxima: a short dependency chain
+                float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
                 for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[sub][rr]);
+                    for (int rr = 0; rr < 16; ++rr) m4[rr & 3] = fmaxf(m4[rr & 3], s[sub][rr]);
+                float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
                 mx = halves_max(mx);
                 const float mt = mx * c;  // this tile's row max, log2 units
                 if (__any(mt > m_ref + kStaleMax)) {
                     const float m_new = fmaxf(m_ref, mt);
                     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                    l_sum *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) l_sum[e] *= alpha;
 #pragma unroll
                     for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
@@ -284,7 +288,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                         const float x1 = __builtin_amdgcn_exp2f(fmaf(s[sub][base + 2 * p + 1], c, -m_use));
                         const uint32_t wv = pack_bf16x2(x0, x1);
                         pk[ks][p] = wv;
-                        l_sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum, false);
+                        l_sum[p] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, l_sum[p], false);
                     }
                 }
                 // O^T += V^T P^T; the D/32 accumulator chains alternate
@@ -325,7 +329,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         }
 
         // Epilogue: one division per row; each lane half summed its own keys.
-        const float l_tot = halves_sum(l_sum);
+        const float l_tot = halves_sum((l_sum[0] + l_sum[1]) + (l_sum[2] + l_sum[3]));
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         // O leaves in 16-byte stores (8 consecutive dims per lane, see o_rows16)
         u32x4 ov[D / 32][2];
