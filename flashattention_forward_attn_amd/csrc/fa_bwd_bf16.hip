@@ -457,11 +457,12 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
         }
     };
 
-    // The row's key limit goes out first (the first barrier needs it; loads
-    // complete in order), then Q, dO and the row statistics, which stay in flight
-    // across that barrier and land together with the first K/V tile.  All through
-    // buffer descriptors, rows past N at an offset past the end (they read zeros),
-    // so no load sits in a branch and none waits for another.
+    // With key limits, the row's limit (which the first barrier needs) goes out
+    // first: loads complete in order, so the wait before the barrier covers it
+    // alone.  Q, dO and the row statistics follow; they stay in flight across that
+    // barrier and land together with the first K/V tile.  All go through buffer
+    // descriptors, rows past N at an offset past the end (they read zeros), so no
+    // load sits in a branch and none waits for another.
     const int qrow = qb * kBQ + w * kQPW + col;
     const bool in = qrow < N;
     int lraw = 0;  // the stored key limit of this row
@@ -551,7 +552,7 @@ void kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* 
                 const char* Kc = Ks + 32 * sub * T::kRow;
                 const char* Vc = Vs + 32 * sub * T::kRow;
                 f32x16 s = f32x16{}, dp = f32x16{};
-                // the S and dP chains alternate: 4-5 % faster than the two chains back
+                // the S and dP chains alternate: 1-5 % faster than the two chains back
                 // to back (an explicit schedule of the operand reads gained nothing more)
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
