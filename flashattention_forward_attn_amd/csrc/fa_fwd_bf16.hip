@@ -4,10 +4,9 @@
 // How IO-Awareness Reshaped the Attention Kernel", sections "FlashAttention (v1)"
 // and "FlashAttention-2".  A workgroup owns one block of query rows of one
 // (batch, head) at a time; it streams K/V tiles through LDS, keeps the score tile in
-// matrix-core accumulators, and carries a running row max m, a running row sum
-// l and an unnormalised output accumulator, re-based whenever m moves; O is
-// divided by l once at the end and L = m + log l is written per row.  Scores
-// never reach device memory.
+// matrix-core accumulators, and carries an exponent reference m, a running row
+// sum l and an unnormalised output accumulator; O is divided by l once at the
+// end and L = m + log l is written per row.  Scores never reach device memory.
 //
 // gfx950 design (not the pages' A100/H100 tiling):
 //   * 8 waves x 32 query rows = 256 rows per query block, two waves per SIMD
@@ -24,12 +23,17 @@
 //     transposes 4x4 blocks of 16-bit values across lanes, and the per-lane source
 //     addresses pick the keys in the accumulator row order of the first
 //     contraction, so no data is permuted anywhere.
-//   * O accumulates per lane for one query, so the rescale by exp2(m_old - m_new)
-//     is a per-lane scalar multiply.  exp2 with log2(e) folded into the scale.
-//   * The reference max only moves when a tile's max exceeds it by more than 8
-//     (log2 units); O / l is unchanged by the choice of reference and P stays
-//     below 2^8 ("FlashAttention 1–4 ...", section "FlashAttention-4",
-//     conditional rescaling).  Most tiles skip the O rescale entirely.
+//   * exp2 with log2(e) folded into the scale.  O / l does not depend on the
+//     exponent reference ("FlashAttention 1–4 ...", section "FlashAttention-4",
+//     conditional rescaling), so each row keeps the max of its first tile as its
+//     reference: no later tile computes a row max, votes or rescales O.  P then
+//     exceeds 1 when later scores are larger; a score 128 or more (log2 units)
+//     above the reference overflows P (and a smaller excess can overflow O for
+//     huge V), which leaves a non-finite sum or output.  The workgroup checks for
+//     that after a block and then computes the block again with the reference
+//     following the running max (moved when a tile's max exceeds it by more than
+//     8, so P stays below 2^8 and O is rescaled by a per-lane scalar: O
+//     accumulates per lane for one query).
 //   * K/V tiles go from global memory straight into LDS (buffer loads with the
 //     LDS bit, 16 bytes per lane, no register staging), double-buffered: the next
 //     tile is in flight while the current one is computed, one barrier per tile.
@@ -68,7 +72,7 @@ constexpr int kBQ = kWaves * kQPW;        // 256 query rows per query block
 // the registers there), 64 at d = 128.
 template <int D>
 constexpr int kBKof = D == 64 ? 128 : 64;
-constexpr float kStaleMax = 8.0f;         // log2 units
+constexpr float kStaleMax = 8.0f;         // log2 units (the recomputation pass moves its reference past this)
 
 template <int D>
 struct Tile {
@@ -93,6 +97,7 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     constexpr int kSub = kBK / 32;  // 32-key slabs per tile
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[2][kWaves];
+    __shared__ int redo_flag[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,8 +221,9 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         float m_ref = -INFINITY;
         float l_sum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: four short dependency chains
 
-        auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
+        auto step = [&](auto stage_c, auto rescale_c, int t) __attribute__((always_inline)) {
             constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
+            constexpr bool RESCALE = decltype(rescale_c)::value;
             if (!kSingleStage && t + 1 < ntiles) dma_tile(kdesc, vdesc, st ^ 1, (t + 1) * kBK);
             const char* Sb = smem + st * T::kStage;
             const int kv0 = t * kBK;
@@ -262,8 +268,10 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                     for (int rr = 0; rr < 16; ++rr) m4[rr & 3] = fmaxf(m4[rr & 3], s[sub][rr]);
                 float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
                 mx = halves_max(mx);
-                const float mt = mx * c;  // this tile's row max, log2 units
-                if (__any(mt > m_ref + kStaleMax)) {
+                const float mt = mx * c;  // this tile's row max, log2 units (first pass: tile 0 only)
+                if constexpr (!RESCALE) {
+                    if (t == 0) m_ref = mt;  // the reference for the whole block
+                } else if (__any(mt > m_ref + kStaleMax)) {
                     const float m_new = fmaxf(m_ref, mt);
                     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
@@ -323,9 +331,43 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                 __syncthreads();
             }
         };
-        for (int t = 0; t < ntiles; t += 2) {
-            step(std::integral_constant<int, 0>{}, t);
-            if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+        auto run = [&](auto rescale_c) __attribute__((always_inline)) {
+            for (int t = 0; t < ntiles; t += 2) {
+                step(std::integral_constant<int, 0>{}, rescale_c, t);
+                if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
+            }
+        };
+        run(std::false_type{});
+        {
+            // The first pass keeps each row's first-tile max as its reference.  A later
+            // score above it by 128 or more (log2 units) overflows P, a smaller excess
+            // can still overflow O, and either leaves a non-finite sum or output; then
+            // the whole workgroup (its barriers stay matched) computes the block again
+            // with the reference following the running max.
+            float chk[4] = {l_sum[0], l_sum[1], l_sum[2], l_sum[3]};
+#pragma unroll
+            for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) chk[rr & 3] = fmaf(oacc[d32][rr], 0.f, chk[rr & 3]);
+            const bool bad = __any(!__builtin_isfinite((chk[0] + chk[1]) + (chk[2] + chk[3])));
+            if (lane == 0) redo_flag[r & 1][w] = bad ? 1 : 0;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            int any_bad = 0;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) any_bad |= redo_flag[r & 1][i];
+            if (any_bad) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+                m_ref = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) l_sum[e] = 0.f;
+                if (ntiles > 0) dma_tile(kdesc, vdesc, 0, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                run(std::true_type{});
+            }
         }
 
         // Epilogue: one division per row; each lane half summed its own keys.

@@ -165,7 +165,7 @@ constexpr int kBQ = kWaves * kQPW;        // 256 query rows per query block
 // half then takes its own exponent)
 template <int D>
 constexpr int kBKof = D == 64 ? 2 * kFp8KTile : kFp8KTile;
-constexpr float kStaleMax = 8.0f;         // log2 units
+constexpr float kStaleMax = 8.0f;         // log2 units (the recomputation pass moves its reference past this)
 
 // K rows of D E4M3 bytes: chunk c of row r sits in slot c ^ kswz(r), so that
 // 16 consecutive rows reading one chunk touch 16 distinct 16-byte bank groups.
@@ -205,6 +205,7 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
     constexpr int kBK = T::kBK, kSub = T::kSub;
     __shared__ __attribute__((aligned(1024))) char smem[2 * T::kStage];
     __shared__ int block_max[2][kWaves];
+    __shared__ int redo_flag[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,8 +397,9 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        auto step = [&](auto stage_c, int t) __attribute__((always_inline)) {
+        auto step = [&](auto stage_c, auto rescale_c, int t) __attribute__((always_inline)) {
             constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
+            constexpr bool RESCALE = decltype(rescale_c)::value;
             if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
             const char* Sb = smem + st * T::kStage;
             const int kv0 = t * kBK;
@@ -450,8 +452,10 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
                 mx = halves_max(mx);
-                const float mt = mx * c;
-                if (__any(mt > m_ref + kStaleMax)) {
+                const float mt = mx * c;  // this tile's row max, log2 units (first pass: tile 0 only)
+                if constexpr (!RESCALE) {
+                    if (t == 0) m_ref = mt;  // the reference for the whole block
+                } else if (__any(mt > m_ref + kStaleMax)) {
                     const float m_new = fmaxf(m_ref, mt);
                     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
                     l_sum *= alpha;
@@ -498,9 +502,41 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                 __syncthreads();
             }
         };
-        for (int t = 0; t < ntiles; t += 2) {
-            step(std::integral_constant<int, 0>{}, t);
-            if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+        auto run = [&](auto rescale_c) __attribute__((always_inline)) {
+            for (int t = 0; t < ntiles; t += 2) {
+                step(std::integral_constant<int, 0>{}, rescale_c, t);
+                if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
+            }
+        };
+        run(std::false_type{});
+        {
+            // As in the bf16 kernel: the first pass keeps each row's first-tile max
+            // as its reference; if that overflowed P or O somewhere in the block (a
+            // non-finite sum or output), the workgroup computes the block again with
+            // the reference following the running max.
+            float chk[4] = {l_sum, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d32 = 0; d32 < D / 32; ++d32)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) chk[rr & 3] = fmaf(oacc[d32][rr], 0.f, chk[rr & 3]);
+            const bool bad = __any(!__builtin_isfinite((chk[0] + chk[1]) + (chk[2] + chk[3])));
+            if (lane == 0) redo_flag[r & 1][w] = bad ? 1 : 0;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            int any_bad = 0;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) any_bad |= redo_flag[r & 1][i];
+            if (any_bad) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+                m_ref = -INFINITY;
+                l_sum = 0.f;
+                if (ntiles > 0) dma_tile(0, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                run(std::true_type{});
+            }
         }
 
         const float l_tot = halves_sum(l_sum);

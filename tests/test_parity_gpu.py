@@ -7,8 +7,12 @@ same seeded inputs, element by element.
   - the five workloads at full size against the full oracle, every element of O
     and every row of LSE, fused and unfused (special rows -- first and last rows,
     tile edges, the diagonal, the masked query block -- also on their own);
-  - determinism, key permutation, fully masked rows and the causal first row.
+  - determinism, key permutation, fully masked rows and the causal first row;
+  - keys whose scores lie far above the first K/V tile's (the fused kernel's
+    exponent reference, and the recomputation of blocks where it overflows).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -121,6 +125,27 @@ def test_workload_full_oracle_large(name):
             assert np.all(np.isneginf(lse[np.broadcast_to(empty[:, None, :], lse.shape)]))
             assert np.all(o[np.broadcast_to(empty[:, None, :], lse.shape)] == 0.0)
         del o, lse
+
+
+@pytest.mark.parametrize("mult", [10.0, 40.0])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_far_above_the_first_tile(causal, d, mult):
+    """K rows of keys 300.. scaled by `mult`: their scores exceed every score of the
+    first K/V tile by about mult x 2.9 standard deviations.  At 10 the fused
+    kernel's first-tile exponent reference leaves P up to ~2^40 (no overflow); at
+    40 the excess passes 128 log2 units, P overflows, and each such block must be
+    recomputed with its reference following the running max."""
+    N = 600
+    w = inputs.custom(f"late_peak_{d}", "bf16", 1, 3, N, d, causal, seed=77 + d)
+    x = inputs.generate(w)
+    k = x.k.copy()
+    k[:, :, 300:, :] *= np.float32(mult)
+    kb = inputs.bf16_bits(k)
+    x = dataclasses.replace(x, k=inputs.bf16_to_f32(kb), k_bits=kb)
+    o, lse = gh.run(x)
+    ro, rl = oracle.attention(x.q, x.k, x.v, causal, w.scale, None, nthreads=gh.oracle_threads())
+    gh.compare("bf16", o, lse, ro, rl, f"fused bf16 late peak x{mult} d={d} causal={causal}")
 
 
 def test_deterministic():
