@@ -25,15 +25,16 @@
 //     contraction, so no data is permuted anywhere.
 //   * exp2 with log2(e) folded into the scale.  O / l does not depend on the
 //     exponent reference ("FlashAttention 1–4 ...", section "FlashAttention-4",
-//     conditional rescaling), so each row keeps the max of its first tile as its
-//     reference: no later tile computes a row max, votes or rescales O.  P then
-//     exceeds 1 when later scores are larger; a score 128 or more (log2 units)
-//     above the reference overflows P (and a smaller excess can overflow O for
-//     huge V), which leaves a non-finite sum or output.  The workgroup checks for
-//     that after a block and then computes the block again with the reference
-//     following the running max (moved when a tile's max exceeds it by more than
-//     8, so P stays below 2^8 and O is rescaled by a per-lane scalar: O
-//     accumulates per lane for one query).
+//     conditional rescaling).  Without key limits each row keeps the max of its
+//     first tile as its reference: no later tile computes a row max, votes or
+//     rescales O.  P then exceeds 1 when later scores are larger; a score 128 or
+//     more (log2 units) above the reference overflows P (and a smaller excess can
+//     overflow O for huge V), which leaves a non-finite sum or output.  The
+//     workgroup checks for that after a block and then computes the block again
+//     with the reference following the running max: moved when a tile's max
+//     exceeds it by more than 8, so P stays below 2^8, and O rescaled by a
+//     per-lane scalar (O accumulates per lane for one query).  With key limits
+//     the reference follows the running max from the start.
 //   * K/V tiles go from global memory straight into LDS (buffer loads with the
 //     LDS bit, 16 bytes per lane, no register staging), double-buffered: the next
 //     tile is in flight while the current one is computed, one barrier per tile.
@@ -337,8 +338,12 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                 if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
             }
         };
-        run(std::false_type{});
-        {
+        // With key limits (the key-padding workload's logits reach ~100 log2 units
+        // of spread per row, and most blocks would overflow a fixed reference) the
+        // reference follows the running max from the start.
+        if constexpr (MASK) run(std::true_type{});
+        if constexpr (!MASK) {
+            run(std::false_type{});
             // The first pass keeps each row's first-tile max as its reference.  A later
             // score above it by 128 or more (log2 units) overflows P, a smaller excess
             // can still overflow O, and either leaves a non-finite sum or output; then

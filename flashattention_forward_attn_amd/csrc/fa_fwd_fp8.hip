@@ -508,9 +508,13 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                 if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
             }
         };
-        run(std::false_type{});
-        {
-            // As in the bf16 kernel: the first pass keeps each row's first-tile max
+        // With key limits (the key-padding workload's logits reach ~100 log2 units
+        // of spread per row, and most blocks would overflow a fixed reference) the
+        // reference follows the running max from the start.
+        if constexpr (MASK) run(std::true_type{});
+        if constexpr (!MASK) {
+            run(std::false_type{});
+            // As in the bf16 kernel (without key limits): the first pass keeps each row's first-tile max
             // as its reference; if that overflowed P or O somewhere in the block (a
             // non-finite sum or output), the workgroup computes the block again with
             // the reference following the running max.
