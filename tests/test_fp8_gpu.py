@@ -97,6 +97,25 @@ def test_fp8_attention_sweep(N, causal, d, mask):
     check(o, lse, ro, rl, f"N={N} causal={causal} d={d} mask={mask}")
 
 
+@pytest.mark.parametrize("mult", [10.0, 40.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_scores_far_above_the_first_tile(causal, mult):
+    """K rows of keys 320.. (whole 64-row code tiles) scaled by `mult`: at 40 their
+    scores overflow the first-tile exponent reference, and the blocks holding such
+    rows must be recomputed with a running reference (as in the bf16 kernel)."""
+    torch = cuda()
+    N, d = 600, 128
+    w = inputs.custom("fp8_late_peak", "bf16", 1, 3, N, d, causal, seed=91)
+    x = inputs.generate(w)
+    k = x.k.copy()
+    k[:, :, 320:, :] *= np.float32(mult)
+    k = inputs.bf16_round(k)
+    signs = inputs.fp8_signs(d, seed=5)
+    o, lse = gpu_attention(torch, x.q, k, x.v, signs, causal, w.scale)
+    ro, rl = oracle_fp8(x.q, k, x.v, signs, causal, w.scale)
+    check(o, lse, ro, rl, f"late peak x{mult} causal={causal}")
+
+
 def test_fp8_outliers_rmse_below_per_tensor_baseline():
     torch = cuda()
     B, H, N, d = 1, 4, 512, 128
