@@ -82,12 +82,17 @@ typedef enum {
 /*
  * Fused forward, bf16 inputs and output, fp32 accumulation and statistics.
  * One kernel: Q tile in registers, K/V tiles streamed through LDS, both
- * contractions on bf16 matrix cores, online softmax (running max, running sum,
- * unnormalised accumulator rescaled per K/V tile, one normalisation at the end);
+ * contractions on bf16 matrix cores, online softmax (an exponent reference per
+ * row, running sum, unnormalised accumulator, one normalisation at the end);
  * the N x N score matrix never reaches device memory ("GPU 与 TPU：让硬件不再是
  * 黑魔法" §11.2-§11.4; "FlashAttention 1–4 ...", sections "FlashAttention (v1)"
- * and "FlashAttention-2").  The probabilities feeding P V are rounded to bf16
- * (nearest-even) and the row sum l is taken over the same rounded values.
+ * and "FlashAttention-2").  Since O / l does not depend on the reference
+ * ("FlashAttention 1–4 ...", section "FlashAttention-4"), without kv_limit each
+ * row keeps its first K/V tile's max as the reference; a block whose sum or
+ * output then overflows is computed again with the reference following the
+ * running max, which kv_limit calls use throughout.  The probabilities feeding
+ * P V are rounded to bf16 (nearest-even) and the row sum l is taken over the
+ * same rounded values.
  */
 fa_status fa_fwd_bf16(const fa_bf16 *q, const fa_bf16 *k, const fa_bf16 *v,
                       fa_bf16 *o, float *lse,
