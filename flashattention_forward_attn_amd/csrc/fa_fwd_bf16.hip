@@ -222,9 +222,10 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         float m_ref = -INFINITY;
         float l_sum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: four short dependency chains
 
-        auto step = [&](auto stage_c, auto rescale_c, int t) __attribute__((always_inline)) {
+        auto step = [&](auto stage_c, auto rescale_c, auto first_c, int t) __attribute__((always_inline)) {
             constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
             constexpr bool RESCALE = decltype(rescale_c)::value;
+            constexpr bool FIRST = decltype(first_c)::value;  // tile 0 of a fixed-reference pass
             if (!kSingleStage && t + 1 < ntiles) dma_tile(kdesc, vdesc, st ^ 1, (t + 1) * kBK);
             const char* Sb = smem + st * T::kStage;
             const int kv0 = t * kBK;
@@ -261,27 +262,29 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                             if (key >= lim) s[sub][rr] = -INFINITY;
                         }
                 }
-                // four independent partial maxima: a short dependency chain
-                float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                if constexpr (RESCALE || FIRST) {
+                    // four independent partial maxima: a short dependency chain
+                    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-                for (int sub = 0; sub < kSub; ++sub)
+                    for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) m4[rr & 3] = fmaxf(m4[rr & 3], s[sub][rr]);
-                float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-                mx = halves_max(mx);
-                const float mt = mx * c;  // this tile's row max, log2 units (first pass: tile 0 only)
-                if constexpr (!RESCALE) {
-                    if (t == 0) m_ref = mt;  // the reference for the whole block
-                } else if (__any(mt > m_ref + kStaleMax)) {
-                    const float m_new = fmaxf(m_ref, mt);
-                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                        for (int rr = 0; rr < 16; ++rr) m4[rr & 3] = fmaxf(m4[rr & 3], s[sub][rr]);
+                    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+                    mx = halves_max(mx);
+                    const float mt = mx * c;  // this tile's row max, log2 units
+                    if constexpr (!RESCALE) {
+                        m_ref = mt;  // the reference for the whole block
+                    } else if (__any(mt > m_ref + kStaleMax)) {
+                        const float m_new = fmaxf(m_ref, mt);
+                        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) l_sum[e] *= alpha;
+                        for (int e = 0; e < 4; ++e) l_sum[e] *= alpha;
 #pragma unroll
-                    for (int d32 = 0; d32 < D / 32; ++d32)
+                        for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-                        for (int rr = 0; rr < 16; ++rr) oacc[d32][rr] *= alpha;
-                    m_ref = m_new;
+                            for (int rr = 0; rr < 16; ++rr) oacc[d32][rr] *= alpha;
+                        m_ref = m_new;
+                    }
                 }
                 const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
@@ -333,9 +336,20 @@ void fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             }
         };
         auto run = [&](auto rescale_c) __attribute__((always_inline)) {
-            for (int t = 0; t < ntiles; t += 2) {
-                step(std::integral_constant<int, 0>{}, rescale_c, t);
-                if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            if constexpr (decltype(rescale_c)::value) {
+                for (int t = 0; t < ntiles; t += 2) {
+                    step(I0{}, rescale_c, std::false_type{}, t);
+                    if (t + 1 < ntiles) step(I1{}, rescale_c, std::false_type{}, t + 1);
+                }
+            } else {
+                // tile 0 sets each row's reference (its row max); later tiles take no max
+                if (ntiles > 0) step(I0{}, rescale_c, std::true_type{}, 0);
+                for (int t = 1; t < ntiles; t += 2) {
+                    step(I1{}, rescale_c, std::false_type{}, t);
+                    if (t + 1 < ntiles) step(I0{}, rescale_c, std::false_type{}, t + 1);
+                }
             }
         };
         // With key limits (the key-padding workload's logits reach ~100 log2 units

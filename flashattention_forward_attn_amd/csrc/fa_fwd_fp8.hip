@@ -397,9 +397,10 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        auto step = [&](auto stage_c, auto rescale_c, int t) __attribute__((always_inline)) {
+        auto step = [&](auto stage_c, auto rescale_c, auto first_c, int t) __attribute__((always_inline)) {
             constexpr int st = kSingleStage ? 0 : decltype(stage_c)::value;
             constexpr bool RESCALE = decltype(rescale_c)::value;
+            constexpr bool FIRST = decltype(first_c)::value;  // tile 0 of a fixed-reference pass
             if (!kSingleStage && t + 1 < ntiles) dma_tile(st ^ 1, (t + 1) * kBK);
             const char* Sb = smem + st * T::kStage;
             const int kv0 = t * kBK;
@@ -446,24 +447,26 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
                             if (key >= lim) s[sub][r] = -INFINITY;
                         }
                 }
-                float mx = -INFINITY;
+                if constexpr (RESCALE || FIRST) {
+                    float mx = -INFINITY;
 #pragma unroll
-                for (int sub = 0; sub < kSub; ++sub)
+                    for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-                mx = halves_max(mx);
-                const float mt = mx * c;  // this tile's row max, log2 units (first pass: tile 0 only)
-                if constexpr (!RESCALE) {
-                    if (t == 0) m_ref = mt;  // the reference for the whole block
-                } else if (__any(mt > m_ref + kStaleMax)) {
-                    const float m_new = fmaxf(m_ref, mt);
-                    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                    l_sum *= alpha;
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+                    mx = halves_max(mx);
+                    const float mt = mx * c;  // this tile's row max, log2 units
+                    if constexpr (!RESCALE) {
+                        m_ref = mt;  // the reference for the whole block
+                    } else if (__any(mt > m_ref + kStaleMax)) {
+                        const float m_new = fmaxf(m_ref, mt);
+                        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                        l_sum *= alpha;
 #pragma unroll
-                    for (int d32 = 0; d32 < D / 32; ++d32)
+                        for (int d32 = 0; d32 < D / 32; ++d32)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
-                    m_ref = m_new;
+                            for (int r = 0; r < 16; ++r) oacc[d32][r] *= alpha;
+                        m_ref = m_new;
+                    }
                 }
                 const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
@@ -503,9 +506,20 @@ void fwd_kernel(const uint8_t* __restrict__ Qc, const int32_t* __restrict__ Qe, 
             }
         };
         auto run = [&](auto rescale_c) __attribute__((always_inline)) {
-            for (int t = 0; t < ntiles; t += 2) {
-                step(std::integral_constant<int, 0>{}, rescale_c, t);
-                if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, rescale_c, t + 1);
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            if constexpr (decltype(rescale_c)::value) {
+                for (int t = 0; t < ntiles; t += 2) {
+                    step(I0{}, rescale_c, std::false_type{}, t);
+                    if (t + 1 < ntiles) step(I1{}, rescale_c, std::false_type{}, t + 1);
+                }
+            } else {
+                // tile 0 sets each row's reference (its row max); later tiles take no max
+                if (ntiles > 0) step(I0{}, rescale_c, std::true_type{}, 0);
+                for (int t = 1; t < ntiles; t += 2) {
+                    step(I1{}, rescale_c, std::false_type{}, t);
+                    if (t + 1 < ntiles) step(I0{}, rescale_c, std::false_type{}, t + 1);
+                }
             }
         };
         // With key limits (the key-padding workload's logits reach ~100 log2 units
